@@ -1,0 +1,157 @@
+"""CPU oracle for the NT MX block-scaled GEMM (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library and its Python binding never import it,
+and it never imports them: the two share no code, tables or helpers.
+
+The arithmetic lives in ``mx_oracle.c`` (plain C, double precision, OpenMP
+over output elements); this module only builds and loads it and marshals
+numpy arrays.  What is computed (see ``mx_oracle.c`` for the citations):
+
+    C[m,n] = sum_kb 2^(sa[m,kb]-127) 2^(sb[n,kb]-127) sum_j dec(A[m,32kb+j]) dec(B[n,32kb+j])
+
+with one E8M0 scale per 32 consecutive K values, A row-major and B
+column-major ("PyTorch 接上 FlyDSL", support matrix row "MXFP 缩放 GEMM" and
+the paragraph under it).
+
+Pins (tests/test_oracle_*.py): E4M3 and E8M0 tables against torch's own
+float8 casts; E2M1 against the E4M3 bit mapping; the GEMM against exact
+rational brute force, float64 matmul of independently decoded operands and
+int64 matmul of integer-valued inputs; scale and sign invariants; the
+double->bf16/fp16 rounding against exact rational nearest-even and torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mx_oracle.c")
+_LIB = os.path.join(_HERE, "libmxoracle.so")
+
+FMT = {"fp8": 0, "fp4": 1}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile mx_oracle.c with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.mx_oracle_decode.argtypes = [ctypes.c_int, P, I64, I64, P]
+    lib.mx_oracle_decode_scale.argtypes = [P, I64, P]
+    lib.mx_oracle_gemm.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, P, P]
+    lib.mx_oracle_gemm_at.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, P, P, I64, P, P]
+    lib.mx_oracle_round_bf16.argtypes = [P, I64, P]
+    lib.mx_oracle_round_f16.argtypes = [P, I64, P]
+    for f in (lib.mx_oracle_decode, lib.mx_oracle_decode_scale, lib.mx_oracle_gemm,
+              lib.mx_oracle_gemm_at, lib.mx_oracle_round_bf16, lib.mx_oracle_round_f16):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u8(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.uint8)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _row_bytes(fmt: str, K: int) -> int:
+    return K // 2 if fmt == "fp4" else K
+
+
+def decode(fmt: str, packed, rows: int, K: int) -> np.ndarray:
+    """Element values of a packed operand, shape [rows, K], float64."""
+    lib = _load()
+    p = _u8(packed)
+    assert p.size == rows * _row_bytes(fmt, K)
+    out = np.empty((rows, K), dtype=np.float64)
+    rc = lib.mx_oracle_decode(FMT[fmt], _ptr(p), rows, K, _ptr(out))
+    if rc:
+        raise ValueError("mx_oracle_decode: %d" % rc)
+    return out
+
+
+def decode_scale(codes) -> np.ndarray:
+    """E8M0 codes -> float64 powers of two (NaN for 0xFF)."""
+    lib = _load()
+    c = _u8(codes)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.mx_oracle_decode_scale(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def _check(fmt, a, b, sa, sb, M, N, K):
+    a, b, sa, sb = _u8(a), _u8(b), _u8(sa), _u8(sb)
+    rb = _row_bytes(fmt, K)
+    if a.size != M * rb or b.size != N * rb or sa.size != M * (K // 32) or sb.size != N * (K // 32):
+        raise ValueError("operand sizes do not match M=%d N=%d K=%d (%s)" % (M, N, K, fmt))
+    return a, b, sa, sb
+
+
+def gemm(fmt: str, a, b, sa, sb, M: int, N: int, K: int):
+    """Full oracle GEMM.  Returns (c, s): float64 [M, N] each, where s is
+    sum_k |a_k b_k| with the scales applied."""
+    lib = _load()
+    a, b, sa, sb = _check(fmt, a, b, sa, sb, M, N, K)
+    c = np.empty((M, N), dtype=np.float64)
+    s = np.empty((M, N), dtype=np.float64)
+    rc = lib.mx_oracle_gemm(FMT[fmt], _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K, _ptr(c), _ptr(s))
+    if rc:
+        raise ValueError("mx_oracle_gemm: %d" % rc)
+    return c, s
+
+
+def gemm_at(fmt: str, a, b, sa, sb, M: int, N: int, K: int, ms, ns):
+    """Oracle values at the listed output positions (ms[i], ns[i])."""
+    lib = _load()
+    a, b, sa, sb = _check(fmt, a, b, sa, sb, M, N, K)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    assert ms.shape == ns.shape
+    c = np.empty(ms.shape, dtype=np.float64)
+    s = np.empty(ms.shape, dtype=np.float64)
+    rc = lib.mx_oracle_gemm_at(FMT[fmt], _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
+                               _ptr(ms), _ptr(ns), ms.size, _ptr(c), _ptr(s))
+    if rc:
+        raise ValueError("mx_oracle_gemm_at: %d" % rc)
+    return c, s
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns (uint16), round-to-nearest-even, direct."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.mx_oracle_round_bf16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def round_f16(x) -> np.ndarray:
+    """float64 -> fp16 bit patterns (uint16), round-to-nearest-even, direct."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.mx_oracle_round_f16(_ptr(x), x.size, _ptr(out))
+    return out
