@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of the NT MX block-scaled GEMM on one MI355X.
+
+One step = one call of the library's default entry point on one batch of
+pre-quantized synthetic input (the pages measure steady-state kernel time
+from already-quantized inputs, excluding compilation and tuning).  Inputs
+are resident in HBM when timing starts; R copies of the operand set are
+rotated so that the rotated footprint (>= 1 GiB) exceeds the 256 MB
+Infinity Cache and every step streams its operands from HBM.
+
+Prints one JSON line with the metric, the roofline fraction of the GEMM
+kernel (HIP events around each launch on the launch stream) and the CPU
+oracle's throughput on the host as a reference baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4/MXFP8 scaled-GEMM TFLOPS on 1 MI355X and % of HBM/MFMA roofline"
+DEFAULT_WORKLOAD = "c2_fp4_32x14336x4096"
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp4": 10066.0, "fp8": 5033.0}   # dense MXFP4 / MXFP8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
+                    help="minimum total bytes of rotated operand sets (0 = one set, cache-hot)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(cs, budget_s):
+    """The oracle, as it stands, on the host cores: whole output rows of the
+    workload, as many as fit the time budget (at least one)."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp:
+        cores = min(cores, int(omp))
+    # calibrate on one row, then run a bounded block of rows; if the whole
+    # workload is cheaper than the budget, repeat it to fill the budget
+    t0 = time.perf_counter()
+    oracle.gemm(cs.fmt, cs.a[:1], cs.b, cs.sa[:1], cs.sb, 1, cs.N, cs.K)
+    t_row = max(time.perf_counter() - t0, 1e-6)
+    rows = int(max(1, min(cs.M, budget_s / t_row)))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemm(cs.fmt, cs.a[:rows], cs.b, cs.sa[:rows], cs.sb, rows, cs.N, cs.K)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or rows < cs.M:
+            break
+    flops = 2.0 * rows * cs.N * cs.K * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d output rows (%d x %d outputs, K=%d) x %d repetitions, %.2f s"
+                      % (rows, cs.M, rows, cs.N, cs.K, reps, dt),
+            "seconds_per_full_workload": dt / reps * cs.M / rows}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mxgen
+    import block_scaled_precision_mm_amd as mx
+
+    torch.cuda.set_device(0)
+    cs = mxgen.case(args.workload)
+    is_fp4 = cs.fmt == "fp4"
+    dev = torch.device("cuda:0")
+    set_bytes = cs.a.nbytes + cs.b.nbytes + cs.sa.nbytes + cs.sb.nbytes + cs.M * cs.N * 2
+    R = 1 if args.rotate_bytes <= 0 else max(1, math.ceil(args.rotate_bytes / set_bytes))
+    R = min(R, 4096)
+    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (cs.a, cs.b, cs.sa, cs.sb)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+    outs = [torch.empty((cs.M, cs.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    wb = mx.mx_scaled_mm_workspace_bytes(is_fp4, cs.M, cs.N, cs.K)
+    ws = torch.zeros(max(wb, 256), dtype=torch.uint8, device=dev)
+    variant, split = mx.mx_default_config(is_fp4, cs.M, cs.N, cs.K, ws.numel())
+    stream = torch.cuda.current_stream()
+    # raw pointers, prepared once: each timed step is one C ABI call
+    entry = mx._lib.mx_scaled_mm_fp4 if is_fp4 else mx._lib.mx_scaled_mm_fp8
+    ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
+            for s_, o in zip(sets, outs)]
+    ws_ptr, ws_len, st_ptr = ws.data_ptr(), ws.numel(), stream.cuda_stream
+
+    def step(i):
+        a, b, sa, sb, c = ptrs[i % R]
+        rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, ws_ptr, ws_len, st_ptr)
+        if rc:
+            raise mx.MxGemmError(rc, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Keep the GPU busy with unrelated work while the host enqueues the timed
+    # steps, so that no step waits for the host: the timed region then holds
+    # back-to-back launches only.
+    filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for _ in range(max(8, K // 4)):
+        filler.add_(1.0)
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    t_enqueue = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s_.elapsed_time(e) for s_, e in ev]
+    span_ms = ev[0][0].elapsed_time(ev[-1][1])
+    ms_per_step = span_ms / K
+    kern_ms = float(np.mean(per_launch_ms))
+    del filler
+
+    flops = cs.flops
+    alg_bytes = cs.algorithmic_bytes(2)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[cs.fmt] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[cs.fmt],
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
+    roof["kernel"] = mx.mx_variant_name(variant) + ("+splitk%d" % split if split > 1 else "")
+    roof["kernel_us"] = round(kern_ms * 1e3, 3)
+    roof["roofline_us"] = round(max(t_hbm, t_mfma) * 1e6, 3)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if is_fp4 else "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": cs.M, "N": cs.N, "K": cs.K,
+                   "operands": "MXFP4 (E2M1) + E8M0/32" if is_fp4 else "MXFP8 (E4M3) + E8M0/32",
+                   "accumulate": "fp32", "out": "bf16", "layout": "NT", "recipe": cs.recipe,
+                   "rotating_sets": R, "variant": mx.mx_variant_name(variant), "split_k": split},
+        "roofline": roof,
+        "wall_s_timed_region": round(wall, 4),
+        "host_enqueue_s": round(t_enqueue, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

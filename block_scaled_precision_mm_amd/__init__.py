@@ -1,0 +1,219 @@
+"""Python binding of the gfx950 NT MX block-scaled GEMM library (libmxgemm.so).
+
+Argument marshalling only: every step of the product runs in the HIP
+kernels of ``csrc/``.  PyTorch supplies device memory and the stream.  The
+functions carry the C ABI's names (see ``include/mxgemm.h``):
+
+    mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace=None, stream=None)
+    mx_scaled_mm_fp8(...)
+    mx_scaled_mm_config(is_fp4, ..., variant, split_k, workspace=None, stream=None)
+    mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
+
+``a``/``b`` are contiguous 1-byte CUDA tensors holding packed codes
+([M, K/2] / [N, K/2] for MXFP4, [M, K] / [N, K] for MXFP8), the scales are
+[M, K/32] / [N, K/32] E8M0 bytes, ``c`` is a contiguous [M, N] tensor of
+the output dtype.  A non-zero status raises MxGemmError (the caller's cue to
+fall back to another implementation).  There is no CPU fallback: if the
+library is missing, importing this package raises.
+
+``scaled_mm`` is the convenience form that allocates C and a zero-filled
+workspace (cached per device) and returns C.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # load torch's HIP runtime first so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
+
+OUT_BF16, OUT_F16, OUT_F32 = 0, 1, 2
+_OUT_OF_DTYPE = {torch.bfloat16: OUT_BF16, torch.float16: OUT_F16, torch.float32: OUT_F32}
+_DTYPE_OF_OUT = {v: k for k, v in _OUT_OF_DTYPE.items()}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmxgemm.so is not built (%s); run __graft_entry__.build() or "
+                      "python block_scaled_precision_mm_amd/build.py" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_INT = ctypes.c_int
+_lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]
+_lib.mx_scaled_mm_fp8.argtypes = _lib.mx_scaled_mm_fp4.argtypes
+_lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT,
+                                     _P, _SZ, _P]
+_lib.mx_scaled_mm_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
+_lib.mx_scaled_mm_workspace_bytes.restype = _SZ
+_lib.mx_config_workspace_bytes.argtypes = [_INT, _INT, _I64, _I64]
+_lib.mx_config_workspace_bytes.restype = _SZ
+_lib.mx_default_config.argtypes = [_INT, _I64, _I64, _I64, _SZ, ctypes.POINTER(_INT), ctypes.POINTER(_INT)]
+_lib.mx_status_string.argtypes = [_INT]
+_lib.mx_status_string.restype = ctypes.c_char_p
+_lib.mx_variant_name.argtypes = [_INT]
+_lib.mx_variant_name.restype = ctypes.c_char_p
+for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
+           "mx_last_hip_error", "mx_abi_version", "mx_default_config"):
+    getattr(_lib, _f).restype = _INT
+
+# every symbol include/mxgemm.h declares
+EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_workspace_bytes",
+           "mx_scaled_mm_config", "mx_config_workspace_bytes", "mx_num_variants",
+           "mx_variant_name", "mx_default_config", "mx_status_string", "mx_last_hip_error",
+           "mx_abi_version")
+
+
+class MxGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.mx_status_string(status).decode()
+        if status == -8:
+            msg += " (hipError %d)" % _lib.mx_last_hip_error()
+        super().__init__("%s: %s (status %d)" % (where, msg, status))
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    if t is None or isinstance(t, int):
+        return 0
+    return t.numel() * t.element_size()
+
+
+def _check_tensors(is_fp4, a, b, sa, sb, c, M, N, K):
+    """Shape/contiguity checks on torch tensors (ints pass through as raw pointers)."""
+    eb = K // 2 if is_fp4 else K
+    for name, t, rows, cols in (("a", a, M, eb), ("b", b, N, eb), ("a_scale", sa, M, K // 32),
+                                ("b_scale", sb, N, K // 32)):
+        if isinstance(t, torch.Tensor):
+            if not t.is_cuda or not t.is_contiguous() or t.element_size() != 1:
+                raise ValueError("%s must be a contiguous 1-byte CUDA tensor" % name)
+            if t.numel() != rows * cols:
+                raise ValueError("%s has %d bytes, expected %d x %d" % (name, t.numel(), rows, cols))
+    if isinstance(c, torch.Tensor):
+        if not c.is_cuda or not c.is_contiguous() or c.numel() != M * N:
+            raise ValueError("c must be a contiguous CUDA tensor with M*N elements")
+
+
+def _out_code(c, out_dtype):
+    if out_dtype is not None:
+        return out_dtype
+    if isinstance(c, torch.Tensor):
+        return _OUT_OF_DTYPE[c.dtype]
+    raise ValueError("out_dtype is required when c is a raw pointer")
+
+
+def mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace=None,
+                     workspace_bytes=None, stream=None) -> None:
+    _check_tensors(True, a, b, a_scale, b_scale, c, M, N, K)
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    st = _lib.mx_scaled_mm_fp4(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
+                               _out_code(c, out_dtype), _ptr(workspace), wb, _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_scaled_mm_fp4")
+
+
+def mx_scaled_mm_fp8(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace=None,
+                     workspace_bytes=None, stream=None) -> None:
+    _check_tensors(False, a, b, a_scale, b_scale, c, M, N, K)
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    st = _lib.mx_scaled_mm_fp8(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
+                               _out_code(c, out_dtype), _ptr(workspace), wb, _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_scaled_mm_fp8")
+
+
+def mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, split_k,
+                        out_dtype=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+    _check_tensors(bool(is_fp4), a, b, a_scale, b_scale, c, M, N, K)
+    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    st = _lib.mx_scaled_mm_config(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                  _ptr(c), M, N, K, _out_code(c, out_dtype), variant, split_k,
+                                  _ptr(workspace), wb, _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_scaled_mm_config")
+
+
+def mx_scaled_mm_workspace_bytes(is_fp4, M, N, K) -> int:
+    return int(_lib.mx_scaled_mm_workspace_bytes(int(bool(is_fp4)), M, N, K))
+
+
+def mx_config_workspace_bytes(variant, split_k, M, N) -> int:
+    return int(_lib.mx_config_workspace_bytes(variant, split_k, M, N))
+
+
+def mx_num_variants() -> int:
+    return int(_lib.mx_num_variants())
+
+
+def mx_variant_name(variant) -> str | None:
+    r = _lib.mx_variant_name(variant)
+    return None if r is None else r.decode()
+
+
+def mx_default_config(is_fp4, M, N, K, workspace_bytes):
+    v, s = _INT(), _INT()
+    st = _lib.mx_default_config(int(bool(is_fp4)), M, N, K, workspace_bytes, ctypes.byref(v), ctypes.byref(s))
+    if st:
+        raise MxGemmError(st, "mx_default_config")
+    return v.value, s.value
+
+
+def mx_status_string(status) -> str:
+    return _lib.mx_status_string(status).decode()
+
+
+def mx_last_hip_error() -> int:
+    return int(_lib.mx_last_hip_error())
+
+
+def mx_abi_version() -> int:
+    return int(_lib.mx_abi_version())
+
+
+# ------------------------------------------------------------- convenience
+_ws_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes on `device`, cached and
+    grown on demand.  Shared by every call on that device: calls that may
+    overlap (different streams) need workspaces of their own."""
+    dev = torch.device(device)
+    with _ws_lock:
+        w = _ws_cache.get(dev)
+        if w is None or w.numel() < nbytes:
+            w = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+            _ws_cache[dev] = w
+        return w
+
+
+def scaled_mm(a, b, a_scale, b_scale, fmt: str, M: int, N: int, K: int,
+              out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """C = MX scaled GEMM of packed operands (fmt 'fp4' or 'fp8'); returns [M, N]."""
+    is_fp4 = fmt == "fp4"
+    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    wb = mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
+    ws = workspace(a.device, wb) if wb else None
+    fn = mx_scaled_mm_fp4 if is_fp4 else mx_scaled_mm_fp8
+    fn(a, b, a_scale, b_scale, c, M, N, K, workspace=ws, stream=stream)
+    return c

@@ -1,0 +1,132 @@
+/*
+ * mxgemm.h -- C ABI of the MI355X (gfx950) NT MX block-scaled GEMM library.
+ *
+ * The operation ("PyTorch 接上 FlyDSL", 5ulink.com, section "支持边界":
+ * support-matrix row "MXFP 缩放 GEMM" and the paragraph under the table;
+ * the devotd.net page, section 2, defines "NT" as left operand row-major,
+ * right operand column-major):
+ *
+ *   C[m,n] = sum_{kb < K/32} 2^(sa[m,kb]-127) * 2^(sb[n,kb]-127)
+ *                           * sum_{j<32} A[m,32kb+j] * B[n,32kb+j]
+ *
+ * with MXFP4 (E2M1) or MXFP8 (E4M3, OCP "FN" flavour) elements, one E8M0
+ * scale per 32 consecutive K values (BlockWise1x32), FP32 accumulation and
+ * BF16 or FP16 output.  K must be a multiple of 128.
+ *
+ * Memory layouts (all device memory, all contiguous, no leading dimensions):
+ *   a        FP4: [M][K/2] bytes, element k of row m in byte m*K/2 + k/2,
+ *                 low nibble when k is even, high nibble when k is odd.
+ *            FP8: [M][K] bytes.
+ *   b        B is K x N column-major, i.e. [N][K/2] (FP4) or [N][K] (FP8)
+ *            bytes, the same packing as a.
+ *   a_scale  [M][K/32] E8M0 bytes, row-major.
+ *   b_scale  [N][K/32] E8M0 bytes, row-major.
+ *   c        [M][N] row-major, element type given by out_dtype; every
+ *            element is overwritten.  c must not overlap any input.
+ *
+ * Ownership and threading: the caller allocates and owns every buffer.  A
+ * call validates its arguments on the host, enqueues its kernels on
+ * `stream` and returns without synchronizing; buffers must stay valid until
+ * that work has completed.  The library allocates no device memory in a
+ * call and keeps no pointer after it returns.  Calls on different streams
+ * may run concurrently as long as they use different workspaces.
+ *
+ * Errors: every function returns an mxg_status_t.  Argument checks happen
+ * before any HIP call, so a rejected call touches no device state.  A
+ * non-zero status means the product was not computed and the caller should
+ * use another implementation (the pages' rule: unsupported combinations
+ * fall back to the original implementation).  Faults inside an enqueued
+ * kernel surface at the caller's next synchronization, as for any HIP work.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; 0 is the null stream of the current device. */
+typedef struct ihipStream_t *mxg_stream_t;
+
+typedef enum {
+    MXG_OUT_BF16 = 0, /* bfloat16, round to nearest even */
+    MXG_OUT_F16 = 1,  /* IEEE half, round to nearest even */
+    MXG_OUT_F32 = 2   /* the FP32 accumulator before output rounding */
+} mxg_out_t;
+
+typedef enum {
+    MXG_OK = 0,
+    MXG_ERR_NULL = -1,      /* a required pointer is NULL */
+    MXG_ERR_SHAPE = -2,     /* M, N or K < 1, or M*N / sizes overflow int64 */
+    MXG_ERR_K_ALIGN = -3,   /* K is not a multiple of 128 */
+    MXG_ERR_PTR_ALIGN = -4, /* a, b or c is not 16-byte aligned; a scale pointer not 4-byte aligned */
+    MXG_ERR_DTYPE = -5,     /* out_dtype is not an mxg_out_t */
+    MXG_ERR_WORKSPACE = -6, /* a forced configuration needs more workspace than given */
+    MXG_ERR_DEVICE = -7,    /* the current device is not gfx950 */
+    MXG_ERR_HIP = -8,       /* a HIP call failed (see mx_last_hip_error) */
+    MXG_ERR_CONFIG = -9     /* an explicit kernel configuration is invalid */
+} mxg_status_t;
+
+/*
+ * MXFP4 (E2M1) x MXFP4 NT scaled GEMM.  Arguments as described above.
+ *
+ * workspace / workspace_bytes: optional device scratch for the split-K
+ * path (partial FP32 tiles and per-tile counters).  It must be zero-filled
+ * once after allocation and 256-byte aligned; the kernels leave its
+ * counters zero again when they finish.  If it is
+ * NULL or smaller than mx_scaled_mm_workspace_bytes(), the call runs
+ * without split-K: the result is the same up to FP32 accumulation order,
+ * possibly slower.  One workspace must not be shared by calls that can run
+ * at the same time.
+ */
+int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
+                     void *workspace, size_t workspace_bytes, mxg_stream_t stream);
+
+/* MXFP8 (E4M3) x MXFP8 NT scaled GEMM.  Same contract as mx_scaled_mm_fp4. */
+int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
+                     void *workspace, size_t workspace_bytes, mxg_stream_t stream);
+
+/* Workspace bytes that let the default configuration use split-K for this
+ * shape (0 when it never does).  is_fp4: 1 for MXFP4, 0 for MXFP8. */
+size_t mx_scaled_mm_workspace_bytes(int is_fp4, int64_t M, int64_t N, int64_t K);
+
+/* Explicit configuration, for tests and tuning: run kernel variant
+ * `variant` (0 .. mx_num_variants()-1) with `split_k` K-splits (>= 1).
+ * Returns MXG_ERR_CONFIG for an unknown variant or a split count that does
+ * not fit K, MXG_ERR_WORKSPACE if split_k > 1 and the workspace is missing
+ * or too small (mx_config_workspace_bytes gives the size).  Same operand
+ * contract as mx_scaled_mm_fp4/fp8. */
+int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
+                        const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
+                        int out_dtype, int variant, int split_k, void *workspace,
+                        size_t workspace_bytes, mxg_stream_t stream);
+size_t mx_config_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
+int mx_num_variants(void);
+/* Human-readable name of a variant (tile shape), or NULL if out of range. */
+const char *mx_variant_name(int variant);
+
+/* The configuration the default entry points would pick for a shape:
+ * writes the variant and split count; returns MXG_OK or a shape error. */
+int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, size_t workspace_bytes,
+                      int *variant, int *split_k);
+
+/* Static description of a status code; never NULL. */
+const char *mx_status_string(int status);
+
+/* The last HIP error code seen by this thread (0 if none). */
+int mx_last_hip_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int mx_abi_version(void);
+#define MXGEMM_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

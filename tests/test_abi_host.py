@@ -1,0 +1,132 @@
+"""Host-only checks of the C ABI library (no GPU needed).
+
+The library must load and export every function include/mxgemm.h
+declares, and every invalid argument must be rejected with its status code
+before any HIP call (so these run on a machine without a GPU).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+LIB = os.path.join(ROOT, "block_scaled_precision_mm_amd", "libmxgemm.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "mxbuild", os.path.join(ROOT, "block_scaled_precision_mm_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    L = ctypes.CDLL(LIB)
+    P, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    L.mx_scaled_mm_fp4.argtypes = [P, P, P, P, P, I64, I64, I64, INT, P, SZ, P]
+    L.mx_scaled_mm_fp8.argtypes = L.mx_scaled_mm_fp4.argtypes
+    L.mx_scaled_mm_config.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, INT, INT, P, SZ, P]
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_variant_name.restype = ctypes.c_char_p
+    L.mx_scaled_mm_workspace_bytes.restype = SZ
+    L.mx_scaled_mm_workspace_bytes.argtypes = [INT, I64, I64, I64]
+    L.mx_config_workspace_bytes.restype = SZ
+    L.mx_config_workspace_bytes.argtypes = [INT, INT, I64, I64]
+    L.mx_default_config.argtypes = [INT, I64, I64, I64, SZ, ctypes.POINTER(INT), ctypes.POINTER(INT)]
+    return L
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_workspace_bytes",
+                     "mx_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.mx_abi_version() == 1
+    assert lib.mx_num_variants() >= 1
+    for v in range(lib.mx_num_variants()):
+        assert lib.mx_variant_name(v)
+    assert lib.mx_variant_name(lib.mx_num_variants()) is None
+
+
+def test_binding_names_match_header():
+    import importlib
+    import sys
+    sys.path.insert(0, ROOT)
+    pkg = importlib.import_module("block_scaled_precision_mm_amd")
+    for name in declared_functions():
+        assert name in pkg.EXPORTS and hasattr(pkg, name), name
+
+
+A = 0x10000   # fake but aligned device addresses: validation never dereferences them
+
+
+@pytest.mark.parametrize("fn", ["mx_scaled_mm_fp4", "mx_scaled_mm_fp8"])
+@pytest.mark.parametrize("args,status", [
+    ((0, A, A, A, A, 8, 8, 128, 0), -1),          # null a
+    ((A, A, A, 0, A, 8, 8, 128, 0), -1),          # null b_scale
+    ((A, A, A, A, 0, 8, 8, 128, 0), -1),          # null c
+    ((A, A, A, A, A, 0, 8, 128, 0), -2),          # M = 0
+    ((A, A, A, A, A, 8, -1, 128, 0), -2),         # N < 0
+    ((A, A, A, A, A, 8, 8, 0, 0), -2),            # K = 0
+    ((A, A, A, A, A, 8, 8, 96, 0), -3),           # K % 128 != 0
+    ((A, A, A, A, A, 8, 8, 200, 0), -3),
+    ((A + 8, A, A, A, A, 8, 8, 128, 0), -4),      # a not 16-byte aligned
+    ((A, A, A, A, A + 4, 8, 8, 128, 0), -4),      # c not 16-byte aligned
+    ((A, A, A + 2, A, A, 8, 8, 128, 0), -4),      # scale not 4-byte aligned
+    ((A, A, A, A, A, 8, 8, 128, 3), -5),          # bad out dtype
+    ((A, A, A, A, A, 8, 8, 128, -1), -5),
+    ((A, A, A, A, A, 1 << 40, 8, 128, 0), -2),    # M beyond the kernels' index range
+])
+def test_invalid_arguments_rejected_before_any_hip_call(lib, fn, args, status):
+    rc = getattr(lib, fn)(*args, None, 0, None)
+    assert rc == status, (rc, lib.mx_status_string(rc))
+
+
+def test_invalid_configs(lib):
+    ok = (A, A, A, A, A, 64, 64, 512, 0)
+    assert lib.mx_scaled_mm_config(1, *ok, -1, 1, None, 0, None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), 1, None, 0, None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, 0, 0, None, 0, None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, 0, 5, None, 0, None) == -9     # 5 splits > 4 steps
+    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, None, 0, None) == -6     # split-K without workspace
+    need = lib.mx_config_workspace_bytes(0, 2, 64, 64)
+    assert need > 0
+    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, A, need - 1, None) == -6
+    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, A + 16, need, None) == -6  # misaligned workspace
+
+
+def test_status_strings(lib):
+    for s in range(-9, 1):
+        assert lib.mx_status_string(s)
+    assert b"128" in lib.mx_status_string(-3)
+    assert lib.mx_status_string(-1234) == b"unknown status"
+
+
+def test_workspace_query_and_default_config(lib):
+    INT = ctypes.c_int
+    v, s = INT(), INT()
+    # decode shape of the headline workload: split-K only with a workspace
+    assert lib.mx_default_config(1, 32, 14336, 4096, 0, ctypes.byref(v), ctypes.byref(s)) == 0
+    assert s.value == 1
+    wb = lib.mx_scaled_mm_workspace_bytes(1, 32, 14336, 4096)
+    assert lib.mx_default_config(1, 32, 14336, 4096, wb, ctypes.byref(v), ctypes.byref(s)) == 0
+    assert wb == lib.mx_config_workspace_bytes(v.value, s.value, 32, 14336)
+    # a large square never splits
+    assert lib.mx_scaled_mm_workspace_bytes(1, 8192, 8192, 8192) == 0
+    assert lib.mx_default_config(1, 8, 8, 100, 0, ctypes.byref(v), ctypes.byref(s)) == -3

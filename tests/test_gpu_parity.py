@@ -1,0 +1,310 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Every case is seeded; inputs come from mxgen (bytes only), expected values
+from the oracle.  Marked `gpu`: needs an MI355X and the built library.
+"""
+from __future__ import annotations
+
+import functools
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mxgen
+import oracle
+from tests import mxcheck, refdecode
+
+pytestmark = pytest.mark.gpu
+
+OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.fixture(scope="module")
+def mx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_scaled_precision_mm_amd as mx
+    return mx
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(mx, fmt, a, b, sa, sb, M, N, K, out="f32", variant=None, split=1, stream=None,
+        ws=None, inputs_on_device=False):
+    """One call through the C ABI; returns float64 (f32) or uint16 bits (bf16/f16)."""
+    da, db, dsa, dsb = (a, b, sa, sb) if inputs_on_device else (dev(a), dev(b), dev(sa), dev(sb))
+    c = torch.empty((M, N), dtype=OUT[out], device="cuda")
+    is_fp4 = fmt == "fp4"
+    if variant is None:
+        if ws is None:
+            wb = mx.mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
+            ws = torch.zeros(max(wb, 256), dtype=torch.uint8, device="cuda")
+        fn = mx.mx_scaled_mm_fp4 if is_fp4 else mx.mx_scaled_mm_fp8
+        fn(da, db, dsa, dsb, c, M, N, K, workspace=ws, stream=stream)
+    else:
+        if ws is None and split > 1:
+            ws = torch.zeros(mx.mx_config_workspace_bytes(variant, split, M, N), dtype=torch.uint8,
+                             device="cuda")
+        mx.mx_scaled_mm_config(is_fp4, da, db, dsa, dsb, c, M, N, K, variant, split, workspace=ws,
+                               stream=stream)
+    if stream is not None:
+        stream.synchronize()
+    torch.cuda.synchronize()
+    if out == "f32":
+        return c.cpu().numpy().astype(np.float64)
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def quantized(fmt, M, N, K, seed):
+    xa = mxgen.normal_bf16(seed, (M, K))
+    xb = mxgen.normal_bf16(seed + 1, (N, K))
+    a, sa = mxgen.quantize(xa, fmt)
+    b, sb = mxgen.quantize(xb, fmt)
+    return a, b, sa, sb
+
+
+def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, split=1, what=""):
+    cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+    hw8 = mxcheck.t8_full(a, b, sa, sb, M, N, K) if fmt == "fp8" else None
+    c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", variant, split)
+    mxcheck.check_f32(c32, cref, S, K, hw8, what)
+    for kind in ("bf16", "f16"):
+        bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, variant, split)
+        mxcheck.check_rounded(bits, cref, S, K, kind, hw8, what + " " + kind)
+        # the epilogue is exactly round-to-nearest-even of the FP32 accumulator
+        rne = oracle.round_bf16(c32) if kind == "bf16" else oracle.round_f16(c32)
+        fin = ~np.isnan(c32)
+        assert np.array_equal(bits[fin], rne[fin]), what + " " + kind + " != RNE(f32)"
+    return c32
+
+
+SMALL_SHAPES = [(1, 1, 128), (5, 17, 256), (16, 64, 512), (33, 200, 640), (100, 130, 1152),
+                (257, 129, 384)]
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_small_shapes_every_variant(mx, fmt, shape):
+    M, N, K = shape
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=M * 131 + N * 7 + K)
+    print("case", fmt, shape, flush=True)
+    for v in range(mx.mx_num_variants()):
+        for split in (1, 3):
+            if split > K // 128:
+                continue
+            full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v, split=split,
+                       what="%s %s v%d s%d" % (fmt, shape, v, split))
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_default_path_random_codes_wide_scales(mx, fmt):
+    # uniformly random codes (every element code, incl. subnormals) and scales over 2^+-14
+    M, N, K = 70, 90, 1024
+    a, sa = mxgen.random_codes(101, fmt, M, K, 113, 141)
+    b, sb = mxgen.random_codes(102, fmt, N, K, 113, 141)
+    full_check(mx, fmt, a, b, sa, sb, M, N, K, what="random codes " + fmt)
+
+
+def _one_hot(fmt, codes_a, codes_b, K, pos):
+    """Rows of A hold codes_a[m] at K position pos, rows of B codes_b[n]; all else zero."""
+    M, N = len(codes_a), len(codes_b)
+    if fmt == "fp4":
+        A = np.zeros((M, K), np.uint8)
+        B = np.zeros((N, K), np.uint8)
+        A[:, pos] = codes_a
+        B[:, pos] = codes_b
+        A = mxgen.pack_fp4(A)
+        B = mxgen.pack_fp4(B)
+    else:
+        A = np.zeros((M, K), np.uint8)
+        B = np.zeros((N, K), np.uint8)
+        A[:, pos] = codes_a
+        B[:, pos] = codes_b
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    return A, B, sa, sb
+
+
+@pytest.mark.parametrize("pos", [0, 1, 7, 8, 15, 16, 31, 32, 63, 64, 100, 127, 128 + 77, 384 + 33])
+def test_fp4_all_code_pairs_exact(mx, pos):
+    K = 512
+    codes = np.arange(16, dtype=np.uint8)
+    A, B, sa, sb = _one_hot("fp4", codes, codes, K, pos)
+    # a sum that starts from +0 is +0 when every term is a zero (+0 + -0 = +0)
+    exact = np.outer(refdecode.e2m1(codes), refdecode.e2m1(codes)) + 0.0
+    for v in range(mx.mx_num_variants()):
+        c32 = run(mx, "fp4", A, B, sa, sb, 16, 16, K, "f32", variant=v)
+        assert np.array_equal(c32, exact), "variant %d pos %d" % (v, pos)
+        bits = run(mx, "fp4", A, B, sa, sb, 16, 16, K, "bf16", variant=v)
+        assert np.array_equal(bits, oracle.round_bf16(exact))
+
+
+@pytest.mark.parametrize("pos", [0, 9, 17, 40, 70, 127, 256 + 5])
+def test_fp8_all_code_pairs_exact(mx, pos):
+    K = 384
+    codes = np.arange(256, dtype=np.uint8)
+    A, B, sa, sb = _one_hot("fp8", codes, codes, K, pos)
+    va = refdecode.e4m3(codes)
+    exact = np.outer(va, va) + 0.0                 # NaN rows/cols for the two NaN codes; -0 -> +0
+    for v in (0, 3, 4):
+        c32 = run(mx, "fp8", A, B, sa, sb, 256, 256, K, "f32", variant=v)
+        nan = np.isnan(exact)
+        assert np.array_equal(np.isnan(c32), nan)
+        assert np.array_equal(c32[~nan], exact[~nan]), "variant %d pos %d" % (v, pos)
+        bits = run(mx, "fp8", A, B, sa, sb, 256, 256, K, "bf16", variant=v)
+        assert np.array_equal(bits[~nan], oracle.round_bf16(exact)[~nan])
+
+
+def test_fp4_integer_valued_exact(mx):
+    # E2M1 x 2^1 values are integers; sums stay below 2^24, so FP32 is exact
+    M, N, K = 96, 160, 2048
+    a, _ = mxgen.random_codes(7, "fp4", M, K)
+    b, _ = mxgen.random_codes(8, "fp4", N, K)
+    sa = np.full((M, K // 32), 128, np.uint8)
+    sb = np.full((N, K // 32), 128, np.uint8)
+    Ai = (refdecode.values("fp4", a, M, K) * 2).astype(np.int64)
+    Bi = (refdecode.values("fp4", b, N, K) * 2).astype(np.int64)
+    exact = (Ai @ Bi.T).astype(np.float64)
+    for v in range(mx.mx_num_variants()):
+        for split in (1, 4):
+            assert np.array_equal(run(mx, "fp4", a, b, sa, sb, M, N, K, "f32", v, split), exact)
+
+
+def test_fp8_integer_valued_exact(mx):
+    # values in [8, 32): every product is a multiple of 2^(E-6) >= 2^(E-13), so the
+    # E4M3 instruction's run alignment drops nothing and FP32 sums stay exact
+    rng = np.random.default_rng(9)
+    M, N, K = 64, 96, 1024
+    def ints(rows):
+        e = rng.integers(10, 12, size=(rows, K))
+        m = rng.integers(0, 8, size=(rows, K))
+        s = rng.integers(0, 2, size=(rows, K))
+        return ((s << 7) | (e << 3) | m).astype(np.uint8)
+    a, b = ints(M), ints(N)
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    exact = (refdecode.values("fp8", a, M, K).astype(np.int64) @
+             refdecode.values("fp8", b, N, K).astype(np.int64).T).astype(np.float64)
+    for v in range(mx.mx_num_variants()):
+        assert np.array_equal(run(mx, "fp8", a, b, sa, sb, M, N, K, "f32", v, 2), exact)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_power_of_two_scale_shift(mx, fmt):
+    M, N, K = 48, 80, 512
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=5)
+    base = run(mx, fmt, a, b, sa, sb, M, N, K, "f32")
+    for k in (-20, -1, 3, 17):
+        got = run(mx, fmt, a, b, (sa.astype(int) + k).astype(np.uint8), sb, M, N, K, "f32")
+        assert np.array_equal(got, np.ldexp(base, k))
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_nan_scale_and_nan_code(mx, fmt):
+    M, N, K = 20, 36, 256
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=6)
+    sa[3, 5] = 255
+    sb[30, 0] = 255
+    a[7] = 0                      # a NaN scale poisons its block even over zero codes
+    sa[7, 2] = 255
+    if fmt == "fp8":
+        b[12, 99] = 0x7F
+    cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+    for v in range(mx.mx_num_variants()):
+        c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
+        assert np.array_equal(np.isnan(c32), np.isnan(cref)), "variant %d" % v
+        for kind in ("bf16", "f16"):
+            bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, v)
+            assert np.array_equal(np.isnan(mxcheck.bits_to_float(bits, kind)), np.isnan(cref))
+
+
+def test_deterministic_and_split_independent(mx):
+    fmt, M, N, K = "fp4", 32, 2048, 4096
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=12)
+    cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+    r1 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
+    r2 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
+    assert np.array_equal(r1, r2)
+    for split in (1, 2, 5, 16):
+        x1 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", 1, split)
+        x2 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", 1, split)
+        assert np.array_equal(x1, x2), "split %d not deterministic" % split
+        mxcheck.check_f32(x1, cref, S, K, None, "split %d" % split)
+
+
+def test_workspace_reuse_and_streams(mx):
+    s = torch.cuda.Stream()
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for fmt, M, N, K in (("fp8", 64, 1024, 2048), ("fp4", 8, 3000, 1024), ("fp8", 64, 1024, 2048)):
+        a, b, sa, sb = quantized(fmt, M, N, K, seed=M + N)
+        cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+        hw8 = mxcheck.t8_full(a, b, sa, sb, M, N, K) if fmt == "fp8" else None
+        with torch.cuda.stream(s):
+            c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", None, 1, s, ws)
+        mxcheck.check_f32(c32, cref, S, K, hw8, "reuse %s %d" % (fmt, N))
+    # counters are back at zero after every split-K call
+    v, split = mx.mx_default_config(False, 64, 1024, 2048, ws.numel())
+    assert split > 1
+    assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_one_hip_runtime_in_process(mx):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+    libs = {line.split()[-1] for line in maps.splitlines() if "libmxgemm" in line}
+    assert libs, "libmxgemm.so is not mapped"
+
+
+# ----------------------------------------------------------------- workloads
+@functools.lru_cache(maxsize=2)
+def _case(name):
+    return mxgen.case(name)
+
+
+def _sample_positions(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, n)
+    ns = rng.integers(0, N, n)
+    # always include the corners and the last row/column (ragged tails)
+    ms = np.concatenate([ms, [0, M - 1, 0, M - 1]])
+    ns = np.concatenate([ns, [0, 0, N - 1, N - 1]])
+    return ms, ns
+
+
+WORKLOADS_FULL = ["c1_fp4_32x256x256", "c2_fp4_32x14336x4096", "c3_fp8_64x4096x4096"]
+WORKLOADS_SAMPLED = ["c4a_fp8_256x28672x8192", "c4b_fp4_256x28672x8192", "c5_fp4_8192x8192x8192"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS_FULL)
+def test_workload_full_oracle(mx, name):
+    cs = _case(name)
+    print("workload", name, cs.recipe, flush=True)
+    cref, S = oracle.gemm(cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K)
+    c32 = run(mx, cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K, "f32")
+    # the named MXFP8 workloads are held to the strict bound (no hardware term)
+    relmax, _ = mxcheck.check_f32(c32, cref, S, cs.K, None, name)
+    bits = run(mx, cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K, "bf16")
+    mxcheck.check_rounded(bits, cref, S, cs.K, "bf16", None, name)
+    assert np.array_equal(bits, oracle.round_bf16(c32))
+    print(name, "max err/S %.3e" % relmax, flush=True)
+
+
+@pytest.mark.parametrize("name", WORKLOADS_SAMPLED)
+def test_workload_sampled_oracle(mx, name):
+    cs = _case(name)
+    print("workload", name, cs.recipe, flush=True)
+    ms, ns = _sample_positions(cs.M, cs.N, 4096, seed=len(name))
+    cref, S = oracle.gemm_at(cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K, ms, ns)
+    da, db, dsa, dsb = dev(cs.a), dev(cs.b), dev(cs.sa), dev(cs.sb)
+    c32 = run(mx, cs.fmt, da, db, dsa, dsb, cs.M, cs.N, cs.K, "f32", inputs_on_device=True)
+    relmax, _ = mxcheck.check_f32(c32[ms, ns], cref, S, cs.K, None, name)
+    bits = run(mx, cs.fmt, da, db, dsa, dsb, cs.M, cs.N, cs.K, "bf16", inputs_on_device=True)
+    mxcheck.check_rounded(bits[ms, ns], cref, S, cs.K, "bf16", None, name)
+    # whole-output property: BF16 output is the RNE of the FP32 accumulator everywhere
+    assert np.array_equal(bits, oracle.round_bf16(c32))
+    print(name, "max err/S %.3e" % relmax, flush=True)
