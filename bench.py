@@ -97,19 +97,17 @@ def main():
     base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (cs.a, cs.b, cs.sa, cs.sb)]
     sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
     outs = [torch.empty((cs.M, cs.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-    wb = mx.mx_scaled_mm_workspace_bytes(is_fp4, cs.M, cs.N, cs.K)
-    ws = torch.zeros(max(wb, 256), dtype=torch.uint8, device=dev)
-    variant, split = mx.mx_default_config(is_fp4, cs.M, cs.N, cs.K, ws.numel())
+    variant = mx.mx_default_variant(is_fp4, cs.M, cs.N, cs.K)
     stream = torch.cuda.current_stream()
     # raw pointers, prepared once: each timed step is one C ABI call
     entry = mx._lib.mx_scaled_mm_fp4 if is_fp4 else mx._lib.mx_scaled_mm_fp8
     ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
             for s_, o in zip(sets, outs)]
-    ws_ptr, ws_len, st_ptr = ws.data_ptr(), ws.numel(), stream.cuda_stream
+    st_ptr = stream.cuda_stream
 
     def step(i):
         a, b, sa, sb, c = ptrs[i % R]
-        rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, ws_ptr, ws_len, st_ptr)
+        rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
         if rc:
             raise mx.MxGemmError(rc, "bench step")
 
@@ -153,7 +151,7 @@ def main():
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[cs.fmt],
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
-    roof["kernel"] = mx.mx_variant_name(variant) + ("+splitk%d" % split if split > 1 else "")
+    roof["kernel"] = mx.mx_variant_name(variant)
     roof["kernel_us"] = round(kern_ms * 1e3, 3)
     roof["roofline_us"] = round(max(t_hbm, t_mfma) * 1e6, 3)
 
@@ -173,7 +171,7 @@ def main():
         "config": {"workload": args.workload, "M": cs.M, "N": cs.N, "K": cs.K,
                    "operands": "MXFP4 (E2M1) + E8M0/32" if is_fp4 else "MXFP8 (E4M3) + E8M0/32",
                    "accumulate": "fp32", "out": "bf16", "layout": "NT", "recipe": cs.recipe,
-                   "rotating_sets": R, "variant": mx.mx_variant_name(variant), "split_k": split},
+                   "rotating_sets": R, "variant": mx.mx_variant_name(variant)},
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_s": round(t_enqueue, 4),

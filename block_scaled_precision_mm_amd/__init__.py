@@ -4,10 +4,10 @@ Argument marshalling only: every step of the product runs in the HIP
 kernels of ``csrc/``.  PyTorch supplies device memory and the stream.  The
 functions carry the C ABI's names (see ``include/mxgemm.h``):
 
-    mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace=None, stream=None)
+    mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None)
     mx_scaled_mm_fp8(...)
-    mx_scaled_mm_config(is_fp4, ..., variant, split_k, workspace=None, stream=None)
-    mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
+    mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, out_dtype=None, stream=None)
+    mx_default_variant(is_fp4, M, N, K)
 
 ``a``/``b`` are contiguous 1-byte CUDA tensors holding packed codes
 ([M, K/2] / [N, K/2] for MXFP4, [M, K] / [N, K] for MXFP8), the scales are
@@ -16,14 +16,12 @@ the output dtype.  A non-zero status raises MxGemmError (the caller's cue to
 fall back to another implementation).  There is no CPU fallback: if the
 library is missing, importing this package raises.
 
-``scaled_mm`` is the convenience form that allocates C and a zero-filled
-workspace (cached per device) and returns C.
+``scaled_mm`` is the convenience form that allocates C and returns it.
 """
 from __future__ import annotations
 
 import ctypes
 import os
-import threading
 
 import torch  # load torch's HIP runtime first so the library binds to the same one
 
@@ -43,27 +41,21 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _INT = ctypes.c_int
-_lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]
+_lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
 _lib.mx_scaled_mm_fp8.argtypes = _lib.mx_scaled_mm_fp4.argtypes
-_lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT,
-                                     _P, _SZ, _P]
-_lib.mx_scaled_mm_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
-_lib.mx_scaled_mm_workspace_bytes.restype = _SZ
-_lib.mx_config_workspace_bytes.argtypes = [_INT, _INT, _I64, _I64]
-_lib.mx_config_workspace_bytes.restype = _SZ
-_lib.mx_default_config.argtypes = [_INT, _I64, _I64, _I64, _SZ, ctypes.POINTER(_INT), ctypes.POINTER(_INT)]
+_lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
+_lib.mx_default_variant.argtypes = [_INT, _I64, _I64, _I64]
 _lib.mx_status_string.argtypes = [_INT]
 _lib.mx_status_string.restype = ctypes.c_char_p
 _lib.mx_variant_name.argtypes = [_INT]
 _lib.mx_variant_name.restype = ctypes.c_char_p
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
-           "mx_last_hip_error", "mx_abi_version", "mx_default_config"):
+           "mx_last_hip_error", "mx_abi_version", "mx_default_variant"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
-EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_workspace_bytes",
-           "mx_scaled_mm_config", "mx_config_workspace_bytes", "mx_num_variants",
-           "mx_variant_name", "mx_default_config", "mx_status_string", "mx_last_hip_error",
+EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
+           "mx_variant_name", "mx_default_variant", "mx_status_string", "mx_last_hip_error",
            "mx_abi_version")
 
 
@@ -92,12 +84,6 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _nbytes(t) -> int:
-    if t is None or isinstance(t, int):
-        return 0
-    return t.numel() * t.element_size()
-
-
 def _check_tensors(is_fp4, a, b, sa, sb, c, M, N, K):
     """Shape/contiguity checks on torch tensors (ints pass through as raw pointers)."""
     eb = K // 2 if is_fp4 else K
@@ -121,43 +107,36 @@ def _out_code(c, out_dtype):
     raise ValueError("out_dtype is required when c is a raw pointer")
 
 
-def mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace=None,
-                     workspace_bytes=None, stream=None) -> None:
+def mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None) -> None:
     _check_tensors(True, a, b, a_scale, b_scale, c, M, N, K)
-    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     st = _lib.mx_scaled_mm_fp4(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
-                               _out_code(c, out_dtype), _ptr(workspace), wb, _stream(stream))
+                               _out_code(c, out_dtype), _stream(stream))
     if st:
         raise MxGemmError(st, "mx_scaled_mm_fp4")
 
 
-def mx_scaled_mm_fp8(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace=None,
-                     workspace_bytes=None, stream=None) -> None:
+def mx_scaled_mm_fp8(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None) -> None:
     _check_tensors(False, a, b, a_scale, b_scale, c, M, N, K)
-    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     st = _lib.mx_scaled_mm_fp8(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
-                               _out_code(c, out_dtype), _ptr(workspace), wb, _stream(stream))
+                               _out_code(c, out_dtype), _stream(stream))
     if st:
         raise MxGemmError(st, "mx_scaled_mm_fp8")
 
 
-def mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, split_k,
-                        out_dtype=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+def mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, out_dtype=None,
+                        stream=None) -> None:
     _check_tensors(bool(is_fp4), a, b, a_scale, b_scale, c, M, N, K)
-    wb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     st = _lib.mx_scaled_mm_config(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
-                                  _ptr(c), M, N, K, _out_code(c, out_dtype), variant, split_k,
-                                  _ptr(workspace), wb, _stream(stream))
+                                  _ptr(c), M, N, K, _out_code(c, out_dtype), variant, _stream(stream))
     if st:
         raise MxGemmError(st, "mx_scaled_mm_config")
 
 
-def mx_scaled_mm_workspace_bytes(is_fp4, M, N, K) -> int:
-    return int(_lib.mx_scaled_mm_workspace_bytes(int(bool(is_fp4)), M, N, K))
-
-
-def mx_config_workspace_bytes(variant, split_k, M, N) -> int:
-    return int(_lib.mx_config_workspace_bytes(variant, split_k, M, N))
+def mx_default_variant(is_fp4, M, N, K) -> int:
+    v = int(_lib.mx_default_variant(int(bool(is_fp4)), M, N, K))
+    if v < 0:
+        raise MxGemmError(v, "mx_default_variant")
+    return v
 
 
 def mx_num_variants() -> int:
@@ -167,14 +146,6 @@ def mx_num_variants() -> int:
 def mx_variant_name(variant) -> str | None:
     r = _lib.mx_variant_name(variant)
     return None if r is None else r.decode()
-
-
-def mx_default_config(is_fp4, M, N, K, workspace_bytes):
-    v, s = _INT(), _INT()
-    st = _lib.mx_default_config(int(bool(is_fp4)), M, N, K, workspace_bytes, ctypes.byref(v), ctypes.byref(s))
-    if st:
-        raise MxGemmError(st, "mx_default_config")
-    return v.value, s.value
 
 
 def mx_status_string(status) -> str:
@@ -190,30 +161,10 @@ def mx_abi_version() -> int:
 
 
 # ------------------------------------------------------------- convenience
-_ws_lock = threading.Lock()
-_ws_cache: dict = {}
-
-
-def workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes on `device`, cached and
-    grown on demand.  Shared by every call on that device: calls that may
-    overlap (different streams) need workspaces of their own."""
-    dev = torch.device(device)
-    with _ws_lock:
-        w = _ws_cache.get(dev)
-        if w is None or w.numel() < nbytes:
-            w = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
-            _ws_cache[dev] = w
-        return w
-
-
 def scaled_mm(a, b, a_scale, b_scale, fmt: str, M: int, N: int, K: int,
               out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
     """C = MX scaled GEMM of packed operands (fmt 'fp4' or 'fp8'); returns [M, N]."""
-    is_fp4 = fmt == "fp4"
     c = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    wb = mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
-    ws = workspace(a.device, wb) if wb else None
-    fn = mx_scaled_mm_fp4 if is_fp4 else mx_scaled_mm_fp8
-    fn(a, b, a_scale, b_scale, c, M, N, K, workspace=ws, stream=stream)
+    fn = mx_scaled_mm_fp4 if fmt == "fp4" else mx_scaled_mm_fp8
+    fn(a, b, a_scale, b_scale, c, M, N, K, stream=stream)
     return c

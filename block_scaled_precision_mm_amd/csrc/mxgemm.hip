@@ -9,13 +9,13 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
 
 #include "../../include/mxgemm.h"
-#include "mx_direct.hpp"
+#include "mx_stream.hpp"
 
 using namespace mxg;
 
@@ -24,35 +24,48 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 // ------------------------------------------------------------------ variants
-typedef void (*KernelFn)(GemmArgs);
+typedef void (*StreamFn)(StreamArgs);
 
 struct Variant {
     const char *name;
-    int tile_m, tile_n;   // workgroup output tile
-    int threads;
-    // [fmt][out][split]
-    KernelFn fn[2][3][2];
+    int mt, wn, kw;          // 16*mt x 16*wn output tile, kw waves splitting K
+    StreamFn fn[2][3];       // [fmt][out]
 };
 
-#define MXG_FN(F, WM, WN, AM, AN, D, O, S) (&mx_gemm_direct<F, WM, WN, AM, AN, D, O, S>)
-#define MXG_OUTS(F, WM, WN, AM, AN, D)                                                        \
-    {{MXG_FN(F, WM, WN, AM, AN, D, OUT_BF16, false), MXG_FN(F, WM, WN, AM, AN, D, OUT_BF16, true)}, \
-     {MXG_FN(F, WM, WN, AM, AN, D, OUT_F16, false), MXG_FN(F, WM, WN, AM, AN, D, OUT_F16, true)},   \
-     {MXG_FN(F, WM, WN, AM, AN, D, OUT_F32, false), MXG_FN(F, WM, WN, AM, AN, D, OUT_F32, true)}}
-#define MXG_VARIANT(NAME, WM, WN, AM, AN, D8, D4)                                              \
-    {NAME, WM * AM * 16, WN * AN * 16, 64 * AM * AN,                                           \
-     {MXG_OUTS(FMT_FP8, WM, WN, AM, AN, D8), MXG_OUTS(FMT_FP4, WM, WN, AM, AN, D4)}}
+// Ring depth (groups in flight per wave) from a register budget: a ring slot
+// holds 4 steps of every A and B subtile plus their scale codes.
+constexpr int ring_depth(int fmt, int mt, int wn)
+{
+    return (mt + wn) * (fmt == FMT_FP4 ? 20 : 36) <= 80 ? 2 : 1;
+}
+
+#define MXG_SFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O>)
+#define MXG_SOUTS(F, MT, WN, KW) \
+    {MXG_SFN(F, MT, WN, KW, OUT_BF16), MXG_SFN(F, MT, WN, KW, OUT_F16), MXG_SFN(F, MT, WN, KW, OUT_F32)}
+#define MXG_STREAM(MT, WN, KW) \
+    {"stream_" #MT "x" #WN "_k" #KW, MT, WN, KW, {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}}
 
 const Variant kVariants[] = {
-    MXG_VARIANT("direct_16x64_w1x4", 1, 1, 1, 4, 8, 8),
-    MXG_VARIANT("direct_32x64_w1x4", 2, 1, 1, 4, 4, 8),
-    MXG_VARIANT("direct_64x64_w1x4", 4, 1, 1, 4, 4, 8),
-    MXG_VARIANT("direct_64x64_w2x2", 2, 2, 2, 2, 4, 4),
-    MXG_VARIANT("direct_128x128_w2x2", 4, 4, 2, 2, 2, 2),
+    MXG_STREAM(1, 1, 4),
+    MXG_STREAM(1, 2, 4),
+    MXG_STREAM(1, 4, 4),
+    MXG_STREAM(2, 1, 4),
+    MXG_STREAM(2, 2, 4),
+    MXG_STREAM(2, 2, 8),
+    MXG_STREAM(2, 4, 4),
+    MXG_STREAM(2, 4, 8),
+    MXG_STREAM(4, 1, 4),
+    MXG_STREAM(4, 1, 8),
+    MXG_STREAM(4, 2, 8),
+    MXG_STREAM(4, 4, 4),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 // ---------------------------------------------------------------- validation
+// Largest K: every per-workgroup buffer range (at most 64 rows) must stay
+// below 2^31 bytes.
+constexpr int64_t kMaxK = (int64_t)1 << 22;
+
 int validate(const void *a, const void *b, const void *sa, const void *sb, const void *c,
              int64_t M, int64_t N, int64_t K, int out_dtype)
 {
@@ -62,10 +75,10 @@ int validate(const void *a, const void *b, const void *sa, const void *sb, const
         return MXG_ERR_SHAPE;
     if (K % 128 != 0)
         return MXG_ERR_K_ALIGN;
-    // kernels index rows with int and steps with int; sizes in size_t
-    if (M > INT32_MAX || N > INT32_MAX || K / 128 > INT32_MAX / 4)
+    // kernels index rows and columns with int
+    if (M > INT32_MAX || N > INT32_MAX || K > kMaxK)
         return MXG_ERR_SHAPE;
-    if (M > INT64_MAX / N || M > INT64_MAX / K || N > INT64_MAX / K)
+    if (M > INT64_MAX / N)
         return MXG_ERR_SHAPE;
     if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
         return MXG_ERR_PTR_ALIGN;
@@ -106,48 +119,36 @@ int check_device()
 
 // ------------------------------------------------------------ configuration
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t workspace_for(int variant, int split_k, int64_t M, int64_t N)
+int find_variant(int mt, int wn, int kw)
 {
-    if (split_k <= 1)
-        return 0;
-    const Variant &v = kVariants[variant];
-    size_t tiles = (size_t)cdiv(M, v.tile_m) * (size_t)cdiv(N, v.tile_n);
-    return align256(tiles * sizeof(unsigned)) + (size_t)split_k * (size_t)M * (size_t)N * sizeof(float);
+    for (int i = 0; i < kNumVariants; ++i)
+        if (kVariants[i].mt == mt && kVariants[i].wn == wn && kVariants[i].kw == kw)
+            return i;
+    return 0;
 }
 
-int pick_variant(int64_t M)
+// Default tile choice.  The output tile should be as square as the row
+// count allows (per-CU traffic is proportional to tile rows + tile
+// columns), and there should be at least as many workgroups as compute
+// units.
+int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 16) return 0;
-    if (M <= 32) return 1;
-    if (M <= 64) return 2;
-    if (M <= 256) return 3;
-    return 4;
-}
-
-// Enough workgroups to give every SIMD of the 256 CUs about two waves; each
-// split keeps at least four 128-deep steps.
-int pick_splits(int variant, int64_t M, int64_t N, int64_t K)
-{
-    const Variant &v = kVariants[variant];
-    int64_t tiles = cdiv(M, v.tile_m) * cdiv(N, v.tile_n);
-    int64_t waves_per_wg = v.threads / 64;
-    int64_t target_wgs = (256 * 4 * 2 + waves_per_wg - 1) / waves_per_wg;
-    int64_t s = cdiv(target_wgs, tiles);
-    int64_t max_s = (K / 128) / 4;
-    if (s > max_s) s = max_s;
-    if (s > 16) s = 16;
-    if (s < 1) s = 1;
-    return (int)s;
+    (void)K;
+    if (M <= 16)
+        return find_variant(1, N >= 256 * 64 ? 4 : (N >= 256 * 32 ? 2 : 1), 4);
+    if (M <= 32)
+        return find_variant(2, N >= 256 * 32 ? 2 : 1, 4);
+    if (M <= 64)
+        return is_fp4 ? find_variant(2, 2, 8) : find_variant(2, 2, 8);
+    return find_variant(4, 4, 4);
 }
 
 int launch(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
-           int64_t M, int64_t N, int64_t K, int out_dtype, int variant, int split_k,
-           void *workspace, size_t workspace_bytes, hipStream_t stream)
+           int64_t M, int64_t N, int64_t K, int out_dtype, int variant, hipStream_t stream)
 {
     const Variant &v = kVariants[variant];
-    GemmArgs p;
+    StreamArgs p;
     p.a = (const uint8_t *)a;
     p.b = (const uint8_t *)b;
     p.sa = (const uint8_t *)sa;
@@ -155,24 +156,14 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     p.c = c;
     p.M = (int)M;
     p.N = (int)N;
-    p.ksteps = (int)(K / 128);
-    p.splits = split_k;
-    p.part = nullptr;
-    p.cnt = nullptr;
-    const int64_t gx = cdiv(N, v.tile_n), gy = cdiv(M, v.tile_m);
+    p.nsteps = (int)(K / 128);
+    p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
+    p.srow_bytes = (unsigned)(K / 32);
+    const int64_t gx = cdiv(N, 16 * v.wn), gy = cdiv(M, 16 * v.mt);
     if (gx > INT32_MAX || gy > 65535)
         return MXG_ERR_SHAPE;
-    if (split_k > 1) {
-        size_t need = workspace_for(variant, split_k, M, N);
-        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
-            return MXG_ERR_WORKSPACE;
-        size_t tiles = (size_t)gx * (size_t)gy;
-        p.cnt = (unsigned *)workspace;
-        p.part = (float *)((char *)workspace + align256(tiles * sizeof(unsigned)));
-    }
-    KernelFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype][split_k > 1 ? 1 : 0];
-    dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)split_k);
-    hipLaunchKernelGGL(fn, grid, dim3(v.threads), 0, stream, p);
+    StreamFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype];
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(64 * v.kw), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
@@ -182,22 +173,16 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
 }
 
 int run_default(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
-                int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
-                size_t workspace_bytes, hipStream_t stream)
+                int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream)
 {
     int rc = validate(a, b, sa, sb, c, M, N, K, out_dtype);
     if (rc)
         return rc;
-    int variant = pick_variant(M);
-    int s = pick_splits(variant, M, N, K);
-    if (s > 1 && (!workspace || workspace_bytes < workspace_for(variant, s, M, N) ||
-                  ((uintptr_t)workspace & 255u)))
-        s = 1;
     rc = check_device();
     if (rc)
         return rc;
-    return launch(is_fp4, a, b, sa, sb, c, M, N, K, out_dtype, variant, s, workspace,
-                  workspace_bytes, stream);
+    return launch(is_fp4, a, b, sa, sb, c, M, N, K, out_dtype, pick_variant(is_fp4, M, N, K),
+                  stream);
 }
 
 }  // namespace
@@ -205,75 +190,40 @@ int run_default(int is_fp4, const void *a, const void *b, const void *sa, const 
 extern "C" {
 
 int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
-                     size_t workspace_bytes, mxg_stream_t stream)
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream)
 {
-    return run_default(1, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+    return run_default(1, a, b, a_scale, b_scale, c, M, N, K, out_dtype, (hipStream_t)stream);
 }
 
 int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
-                     size_t workspace_bytes, mxg_stream_t stream)
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream)
 {
-    return run_default(0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+    return run_default(0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, (hipStream_t)stream);
 }
 
-size_t mx_scaled_mm_workspace_bytes(int is_fp4, int64_t M, int64_t N, int64_t K)
+int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
-    (void)is_fp4;
-    if (M < 1 || N < 1 || K < 128 || K % 128)
-        return 0;
-    int variant = pick_variant(M);
-    return workspace_for(variant, pick_splits(variant, M, N, K), M, N);
-}
-
-int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, size_t workspace_bytes,
-                      int *variant, int *split_k)
-{
-    (void)is_fp4;
-    if (!variant || !split_k)
-        return MXG_ERR_NULL;
-    if (M < 1 || N < 1 || K < 1)
+    if (M < 1 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX || K > kMaxK)
         return MXG_ERR_SHAPE;
     if (K % 128)
         return MXG_ERR_K_ALIGN;
-    int v = pick_variant(M);
-    int s = pick_splits(v, M, N, K);
-    if (s > 1 && workspace_bytes < workspace_for(v, s, M, N))
-        s = 1;
-    *variant = v;
-    *split_k = s;
-    return MXG_OK;
+    return pick_variant(is_fp4 ? 1 : 0, M, N, K);
 }
 
 int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
-                        int out_dtype, int variant, int split_k, void *workspace,
-                        size_t workspace_bytes, mxg_stream_t stream)
+                        int out_dtype, int variant, mxg_stream_t stream)
 {
     int rc = validate(a, b, a_scale, b_scale, c, M, N, K, out_dtype);
     if (rc)
         return rc;
-    if (variant < 0 || variant >= kNumVariants || split_k < 1 || split_k > K / 128 ||
-        split_k > 65535)
+    if (variant < 0 || variant >= kNumVariants)
         return MXG_ERR_CONFIG;
-    if (split_k > 1 && (!workspace || workspace_bytes < workspace_for(variant, split_k, M, N) ||
-                        ((uintptr_t)workspace & 255u)))
-        return MXG_ERR_WORKSPACE;
     rc = check_device();
     if (rc)
         return rc;
-    return launch(is_fp4, a, b, a_scale, b_scale, c, M, N, K, out_dtype, variant, split_k,
-                  workspace, workspace_bytes, (hipStream_t)stream);
-}
-
-size_t mx_config_workspace_bytes(int variant, int split_k, int64_t M, int64_t N)
-{
-    if (variant < 0 || variant >= kNumVariants || M < 1 || N < 1)
-        return 0;
-    return workspace_for(variant, split_k, M, N);
+    return launch(is_fp4 ? 1 : 0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, variant,
+                  (hipStream_t)stream);
 }
 
 int mx_num_variants(void) { return kNumVariants; }
@@ -294,10 +244,9 @@ const char *mx_status_string(int status)
     case MXG_ERR_K_ALIGN: return "K is not a multiple of 128";
     case MXG_ERR_PTR_ALIGN: return "misaligned pointer (operands and C need 16 bytes, scales 4 bytes)";
     case MXG_ERR_DTYPE: return "unknown output dtype";
-    case MXG_ERR_WORKSPACE: return "workspace missing, misaligned or too small for the requested split-K";
     case MXG_ERR_DEVICE: return "current device is not gfx950";
     case MXG_ERR_HIP: return "HIP runtime error";
-    case MXG_ERR_CONFIG: return "invalid kernel variant or split count";
+    case MXG_ERR_CONFIG: return "invalid kernel variant";
     default: return "unknown status";
     }
 }

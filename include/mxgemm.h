@@ -29,7 +29,7 @@
  * `stream` and returns without synchronizing; buffers must stay valid until
  * that work has completed.  The library allocates no device memory in a
  * call and keeps no pointer after it returns.  Calls on different streams
- * may run concurrently as long as they use different workspaces.
+ * may run concurrently.
  *
  * Errors: every function returns an mxg_status_t.  Argument checks happen
  * before any HIP call, so a rejected call touches no device state.  A
@@ -60,60 +60,57 @@ typedef enum {
 typedef enum {
     MXG_OK = 0,
     MXG_ERR_NULL = -1,      /* a required pointer is NULL */
-    MXG_ERR_SHAPE = -2,     /* M, N or K < 1, or M*N / sizes overflow int64 */
+    MXG_ERR_SHAPE = -2,     /* M, N or K < 1, K > 2^22, M or N > 2^31-1, or M*N overflows int64 */
     MXG_ERR_K_ALIGN = -3,   /* K is not a multiple of 128 */
     MXG_ERR_PTR_ALIGN = -4, /* a, b or c is not 16-byte aligned; a scale pointer not 4-byte aligned */
     MXG_ERR_DTYPE = -5,     /* out_dtype is not an mxg_out_t */
-    MXG_ERR_WORKSPACE = -6, /* a forced configuration needs more workspace than given */
     MXG_ERR_DEVICE = -7,    /* the current device is not gfx950 */
     MXG_ERR_HIP = -8,       /* a HIP call failed (see mx_last_hip_error) */
-    MXG_ERR_CONFIG = -9     /* an explicit kernel configuration is invalid */
+    MXG_ERR_CONFIG = -9     /* an explicit kernel variant is invalid */
 } mxg_status_t;
 
 /*
- * MXFP4 (E2M1) x MXFP4 NT scaled GEMM.  Arguments as described above.
+ * MXFP4 (E2M1) x MXFP4 NT scaled GEMM: C = A * B^T as defined above.
  *
- * workspace / workspace_bytes: optional device scratch for the split-K
- * path (partial FP32 tiles and per-tile counters).  It must be zero-filled
- * once after allocation and 256-byte aligned; the kernels leave its
- * counters zero again when they finish.  If it is
- * NULL or smaller than mx_scaled_mm_workspace_bytes(), the call runs
- * without split-K: the result is the same up to FP32 accumulation order,
- * possibly slower.  One workspace must not be shared by calls that can run
- * at the same time.
+ * a, b         packed E2M1 codes, [M][K/2] and [N][K/2] bytes, 16-byte aligned.
+ * a_scale      E8M0 codes [M][K/32], 4-byte aligned.
+ * b_scale      E8M0 codes [N][K/32], 4-byte aligned.
+ * c            [M][N] output of type out_dtype, 16-byte aligned.
+ * M, N, K      logical sizes (K counts elements, not bytes); M, N >= 1,
+ *              K a positive multiple of 128 and at most 2^22.
+ * out_dtype    an mxg_out_t.
+ * stream       HIP stream the work is enqueued on (0 = null stream).
+ *
+ * Returns MXG_OK after enqueueing, or an error status with nothing
+ * enqueued.  No workspace is needed: the kernels never communicate between
+ * workgroups.
  */
 int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
                      void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
-                     void *workspace, size_t workspace_bytes, mxg_stream_t stream);
+                     mxg_stream_t stream);
 
-/* MXFP8 (E4M3) x MXFP8 NT scaled GEMM.  Same contract as mx_scaled_mm_fp4. */
+/* MXFP8 (E4M3) x MXFP8 NT scaled GEMM.  Same contract as mx_scaled_mm_fp4
+ * except that a and b hold one E4M3 code per byte: [M][K] and [N][K]. */
 int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
                      void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
-                     void *workspace, size_t workspace_bytes, mxg_stream_t stream);
+                     mxg_stream_t stream);
 
-/* Workspace bytes that let the default configuration use split-K for this
- * shape (0 when it never does).  is_fp4: 1 for MXFP4, 0 for MXFP8. */
-size_t mx_scaled_mm_workspace_bytes(int is_fp4, int64_t M, int64_t N, int64_t K);
-
-/* Explicit configuration, for tests and tuning: run kernel variant
- * `variant` (0 .. mx_num_variants()-1) with `split_k` K-splits (>= 1).
- * Returns MXG_ERR_CONFIG for an unknown variant or a split count that does
- * not fit K, MXG_ERR_WORKSPACE if split_k > 1 and the workspace is missing
- * or too small (mx_config_workspace_bytes gives the size).  Same operand
- * contract as mx_scaled_mm_fp4/fp8. */
+/* Explicit kernel variant, for tests and tuning: run variant `variant`
+ * (0 .. mx_num_variants()-1) instead of the one the default entry points
+ * pick.  is_fp4: 1 for MXFP4 operands, 0 for MXFP8.  Same operand contract
+ * and errors as mx_scaled_mm_fp4/fp8, plus MXG_ERR_CONFIG for an unknown
+ * variant.  Every variant computes the same product; they differ in tiling
+ * and therefore in FP32 accumulation order. */
 int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
-                        int out_dtype, int variant, int split_k, void *workspace,
-                        size_t workspace_bytes, mxg_stream_t stream);
-size_t mx_config_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
+                        int out_dtype, int variant, mxg_stream_t stream);
 int mx_num_variants(void);
 /* Human-readable name of a variant (tile shape), or NULL if out of range. */
 const char *mx_variant_name(int variant);
 
-/* The configuration the default entry points would pick for a shape:
- * writes the variant and split count; returns MXG_OK or a shape error. */
-int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, size_t workspace_bytes,
-                      int *variant, int *split_k);
+/* The variant the default entry points pick for a shape (>= 0), or a
+ * negative status for an invalid shape. */
+int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
 
 /* Static description of a status code; never NULL. */
 const char *mx_status_string(int status);
@@ -123,7 +120,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 1
+#define MXGEMM_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

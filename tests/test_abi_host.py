@@ -27,17 +27,13 @@ def lib():
         spec.loader.exec_module(mod)
         mod.build()
     L = ctypes.CDLL(LIB)
-    P, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
-    L.mx_scaled_mm_fp4.argtypes = [P, P, P, P, P, I64, I64, I64, INT, P, SZ, P]
+    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.mx_scaled_mm_fp4.argtypes = [P, P, P, P, P, I64, I64, I64, INT, P]
     L.mx_scaled_mm_fp8.argtypes = L.mx_scaled_mm_fp4.argtypes
-    L.mx_scaled_mm_config.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, INT, INT, P, SZ, P]
+    L.mx_scaled_mm_config.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, INT, P]
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_variant_name.restype = ctypes.c_char_p
-    L.mx_scaled_mm_workspace_bytes.restype = SZ
-    L.mx_scaled_mm_workspace_bytes.argtypes = [INT, I64, I64, I64]
-    L.mx_config_workspace_bytes.restype = SZ
-    L.mx_config_workspace_bytes.argtypes = [INT, INT, I64, I64]
-    L.mx_default_config.argtypes = [INT, I64, I64, I64, SZ, ctypes.POINTER(INT), ctypes.POINTER(INT)]
+    L.mx_default_variant.argtypes = [INT, I64, I64, I64]
     return L
 
 
@@ -49,7 +45,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_workspace_bytes",
+    for required in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config",
                      "mx_status_string"):
         assert required in names
 
@@ -57,7 +53,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 1
+    assert lib.mx_abi_version() == 2
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -92,41 +88,36 @@ A = 0x10000   # fake but aligned device addresses: validation never dereferences
     ((A, A, A, A, A, 8, 8, 128, 3), -5),          # bad out dtype
     ((A, A, A, A, A, 8, 8, 128, -1), -5),
     ((A, A, A, A, A, 1 << 40, 8, 128, 0), -2),    # M beyond the kernels' index range
+    ((A, A, A, A, A, 8, 1 << 31, 128, 0), -2),    # N beyond the kernels' index range
+    ((A, A, A, A, A, 8, 8, (1 << 22) + 128, 0), -2),  # K beyond the per-workgroup buffer range
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(lib, fn, args, status):
-    rc = getattr(lib, fn)(*args, None, 0, None)
+    rc = getattr(lib, fn)(*args, None)
     assert rc == status, (rc, lib.mx_status_string(rc))
 
 
 def test_invalid_configs(lib):
     ok = (A, A, A, A, A, 64, 64, 512, 0)
-    assert lib.mx_scaled_mm_config(1, *ok, -1, 1, None, 0, None) == -9
-    assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), 1, None, 0, None) == -9
-    assert lib.mx_scaled_mm_config(1, *ok, 0, 0, None, 0, None) == -9
-    assert lib.mx_scaled_mm_config(1, *ok, 0, 5, None, 0, None) == -9     # 5 splits > 4 steps
-    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, None, 0, None) == -6     # split-K without workspace
-    need = lib.mx_config_workspace_bytes(0, 2, 64, 64)
-    assert need > 0
-    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, A, need - 1, None) == -6
-    assert lib.mx_scaled_mm_config(1, *ok, 0, 2, A + 16, need, None) == -6  # misaligned workspace
+    assert lib.mx_scaled_mm_config(1, *ok, -1, None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), None) == -9
+    # argument errors take precedence over the variant check
+    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 64, 64, 500, 0, 0, None) == -3
+    assert lib.mx_scaled_mm_config(0, 0, A, A, A, A, 64, 64, 512, 0, 0, None) == -1
 
 
 def test_status_strings(lib):
-    for s in range(-9, 1):
-        assert lib.mx_status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -7, -8, -9):
+        assert lib.mx_status_string(s) != b"unknown status"
     assert b"128" in lib.mx_status_string(-3)
     assert lib.mx_status_string(-1234) == b"unknown status"
 
 
-def test_workspace_query_and_default_config(lib):
-    INT = ctypes.c_int
-    v, s = INT(), INT()
-    # decode shape of the headline workload: split-K only with a workspace
-    assert lib.mx_default_config(1, 32, 14336, 4096, 0, ctypes.byref(v), ctypes.byref(s)) == 0
-    assert s.value == 1
-    wb = lib.mx_scaled_mm_workspace_bytes(1, 32, 14336, 4096)
-    assert lib.mx_default_config(1, 32, 14336, 4096, wb, ctypes.byref(v), ctypes.byref(s)) == 0
-    assert wb == lib.mx_config_workspace_bytes(v.value, s.value, 32, 14336)
-    # a large square never splits
-    assert lib.mx_scaled_mm_workspace_bytes(1, 8192, 8192, 8192) == 0
-    assert lib.mx_default_config(1, 8, 8, 100, 0, ctypes.byref(v), ctypes.byref(s)) == -3
+def test_default_variant(lib):
+    n = lib.mx_num_variants()
+    for shape in ((1, 4096, 4096), (32, 14336, 4096), (64, 4096, 4096), (256, 28672, 8192),
+                  (8192, 8192, 8192), (7, 3, 128)):
+        for is4 in (0, 1):
+            v = lib.mx_default_variant(is4, *shape)
+            assert 0 <= v < n, (shape, v)
+    assert lib.mx_default_variant(1, 8, 8, 100) == -3
+    assert lib.mx_default_variant(1, 0, 8, 128) == -2

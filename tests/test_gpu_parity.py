@@ -33,24 +33,17 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def run(mx, fmt, a, b, sa, sb, M, N, K, out="f32", variant=None, split=1, stream=None,
-        ws=None, inputs_on_device=False):
+def run(mx, fmt, a, b, sa, sb, M, N, K, out="f32", variant=None, stream=None,
+        inputs_on_device=False):
     """One call through the C ABI; returns float64 (f32) or uint16 bits (bf16/f16)."""
     da, db, dsa, dsb = (a, b, sa, sb) if inputs_on_device else (dev(a), dev(b), dev(sa), dev(sb))
     c = torch.empty((M, N), dtype=OUT[out], device="cuda")
     is_fp4 = fmt == "fp4"
     if variant is None:
-        if ws is None:
-            wb = mx.mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
-            ws = torch.zeros(max(wb, 256), dtype=torch.uint8, device="cuda")
         fn = mx.mx_scaled_mm_fp4 if is_fp4 else mx.mx_scaled_mm_fp8
-        fn(da, db, dsa, dsb, c, M, N, K, workspace=ws, stream=stream)
+        fn(da, db, dsa, dsb, c, M, N, K, stream=stream)
     else:
-        if ws is None and split > 1:
-            ws = torch.zeros(mx.mx_config_workspace_bytes(variant, split, M, N), dtype=torch.uint8,
-                             device="cuda")
-        mx.mx_scaled_mm_config(is_fp4, da, db, dsa, dsb, c, M, N, K, variant, split, workspace=ws,
-                               stream=stream)
+        mx.mx_scaled_mm_config(is_fp4, da, db, dsa, dsb, c, M, N, K, variant, stream=stream)
     if stream is not None:
         stream.synchronize()
     torch.cuda.synchronize()
@@ -67,13 +60,13 @@ def quantized(fmt, M, N, K, seed):
     return a, b, sa, sb
 
 
-def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, split=1, what=""):
+def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, what=""):
     cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
     hw8 = mxcheck.t8_full(a, b, sa, sb, M, N, K) if fmt == "fp8" else None
-    c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", variant, split)
+    c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", variant)
     mxcheck.check_f32(c32, cref, S, K, hw8, what)
     for kind in ("bf16", "f16"):
-        bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, variant, split)
+        bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, variant)
         mxcheck.check_rounded(bits, cref, S, K, kind, hw8, what + " " + kind)
         # the epilogue is exactly round-to-nearest-even of the FP32 accumulator
         rne = oracle.round_bf16(c32) if kind == "bf16" else oracle.round_f16(c32)
@@ -82,8 +75,11 @@ def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, split=1, what=""):
     return c32
 
 
-SMALL_SHAPES = [(1, 1, 128), (5, 17, 256), (16, 64, 512), (33, 200, 640), (100, 130, 1152),
-                (257, 129, 384)]
+# K/128 = 1, 2, 3 (no whole 4-step group), 4 (one group, fewer groups than
+# waves), 5 and 9 (a group run plus a leftover step), 12, 16 (several groups
+# per wave); M and N ragged against every tile size
+SMALL_SHAPES = [(1, 1, 128), (5, 17, 256), (257, 129, 384), (16, 64, 512), (33, 200, 640),
+                (100, 130, 1152), (70, 47, 1536), (3, 1000, 2048)]
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
@@ -93,11 +89,8 @@ def test_small_shapes_every_variant(mx, fmt, shape):
     a, b, sa, sb = quantized(fmt, M, N, K, seed=M * 131 + N * 7 + K)
     print("case", fmt, shape, flush=True)
     for v in range(mx.mx_num_variants()):
-        for split in (1, 3):
-            if split > K // 128:
-                continue
-            full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v, split=split,
-                       what="%s %s v%d s%d" % (fmt, shape, v, split))
+        full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v,
+                   what="%s %s %s" % (fmt, shape, mx.mx_variant_name(v)))
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
@@ -150,7 +143,7 @@ def test_fp8_all_code_pairs_exact(mx, pos):
     A, B, sa, sb = _one_hot("fp8", codes, codes, K, pos)
     va = refdecode.e4m3(codes)
     exact = np.outer(va, va) + 0.0                 # NaN rows/cols for the two NaN codes; -0 -> +0
-    for v in (0, 3, 4):
+    for v in range(mx.mx_num_variants()):
         c32 = run(mx, "fp8", A, B, sa, sb, 256, 256, K, "f32", variant=v)
         nan = np.isnan(exact)
         assert np.array_equal(np.isnan(c32), nan)
@@ -170,8 +163,7 @@ def test_fp4_integer_valued_exact(mx):
     Bi = (refdecode.values("fp4", b, N, K) * 2).astype(np.int64)
     exact = (Ai @ Bi.T).astype(np.float64)
     for v in range(mx.mx_num_variants()):
-        for split in (1, 4):
-            assert np.array_equal(run(mx, "fp4", a, b, sa, sb, M, N, K, "f32", v, split), exact)
+        assert np.array_equal(run(mx, "fp4", a, b, sa, sb, M, N, K, "f32", v), exact)
 
 
 def test_fp8_integer_valued_exact(mx):
@@ -190,7 +182,7 @@ def test_fp8_integer_valued_exact(mx):
     exact = (refdecode.values("fp8", a, M, K).astype(np.int64) @
              refdecode.values("fp8", b, N, K).astype(np.int64).T).astype(np.float64)
     for v in range(mx.mx_num_variants()):
-        assert np.array_equal(run(mx, "fp8", a, b, sa, sb, M, N, K, "f32", v, 2), exact)
+        assert np.array_equal(run(mx, "fp8", a, b, sa, sb, M, N, K, "f32", v), exact)
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
@@ -222,34 +214,29 @@ def test_nan_scale_and_nan_code(mx, fmt):
             assert np.array_equal(np.isnan(mxcheck.bits_to_float(bits, kind)), np.isnan(cref))
 
 
-def test_deterministic_and_split_independent(mx):
+def test_deterministic(mx):
     fmt, M, N, K = "fp4", 32, 2048, 4096
     a, b, sa, sb = quantized(fmt, M, N, K, seed=12)
     cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
     r1 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
     r2 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
     assert np.array_equal(r1, r2)
-    for split in (1, 2, 5, 16):
-        x1 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", 1, split)
-        x2 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", 1, split)
-        assert np.array_equal(x1, x2), "split %d not deterministic" % split
-        mxcheck.check_f32(x1, cref, S, K, None, "split %d" % split)
+    for v in range(mx.mx_num_variants()):
+        x1 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
+        x2 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
+        assert np.array_equal(x1, x2), "%s not deterministic" % mx.mx_variant_name(v)
+        mxcheck.check_f32(x1, cref, S, K, None, mx.mx_variant_name(v))
 
 
-def test_workspace_reuse_and_streams(mx):
+def test_streams(mx):
     s = torch.cuda.Stream()
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
-    for fmt, M, N, K in (("fp8", 64, 1024, 2048), ("fp4", 8, 3000, 1024), ("fp8", 64, 1024, 2048)):
+    for fmt, M, N, K in (("fp8", 64, 1024, 2048), ("fp4", 8, 3000, 1024), ("fp8", 40, 1000, 4608)):
         a, b, sa, sb = quantized(fmt, M, N, K, seed=M + N)
         cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
         hw8 = mxcheck.t8_full(a, b, sa, sb, M, N, K) if fmt == "fp8" else None
         with torch.cuda.stream(s):
-            c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", None, 1, s, ws)
-        mxcheck.check_f32(c32, cref, S, K, hw8, "reuse %s %d" % (fmt, N))
-    # counters are back at zero after every split-K call
-    v, split = mx.mx_default_config(False, 64, 1024, 2048, ws.numel())
-    assert split > 1
-    assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0
+            c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", None, s)
+        mxcheck.check_f32(c32, cref, S, K, hw8, "stream %s %d" % (fmt, N))
 
 
 def test_one_hip_runtime_in_process(mx):
