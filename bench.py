@@ -1,16 +1,17 @@
 #!/usr/bin/env python3
 """Throughput of the NT MX block-scaled GEMM on one MI355X.
 
-One step = one call of the library's default entry point on one batch of
-pre-quantized synthetic input (the pages measure steady-state kernel time
+One step = one call of the library's default entry point (one kernel
+launch) on one batch of pre-quantized synthetic input (the pages measure steady-state kernel time
 from already-quantized inputs, excluding compilation and tuning).  Inputs
 are resident in HBM when timing starts; R copies of the operand set are
 rotated so that the rotated footprint (>= 1 GiB) exceeds the 256 MB
 Infinity Cache and every step streams its operands from HBM.
 
 Prints one JSON line with the metric, the roofline fraction of the GEMM
-kernel (HIP events around each launch on the launch stream) and the CPU
-oracle's throughput on the host as a reference baseline.
+kernel (its average duration from HIP events around the K back-to-back
+launches, on the launch stream) and the CPU oracle's throughput on the host
+as a reference baseline.
 """
 from __future__ import annotations
 
@@ -41,7 +42,53 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the GEMM, run a plain device-to-device copy of BYTES bytes "
+                         "--steps times (reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources of the library: counter-derived traffic
+    figures are only reported for the kernels they were measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_precision_mm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, variant_name):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (profiles/traffic.json), or None when they were taken on other kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_digest") != kernel_source_digest() or rec.get("kernel") != variant_name:
+        return None
+    return rec
+
+
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of a known size, for counter scaling."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps, "ms_per_copy": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
 def cpu_baseline(cs, budget_s):
@@ -81,6 +128,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import numpy as np
     import torch
 
@@ -117,25 +167,25 @@ def main():
 
     # Keep the GPU busy with unrelated work while the host enqueues the timed
     # steps, so that no step waits for the host: the timed region then holds
-    # back-to-back launches only.
+    # K back-to-back launches of the GEMM on `stream`, bracketed by two HIP
+    # events recorded on that same stream.
     filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     for _ in range(max(8, K // 4)):
         filler.add_(1.0)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(args.warmup + i)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     t_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [s_.elapsed_time(e) for s_, e in ev]
-    span_ms = ev[0][0].elapsed_time(ev[-1][1])
+    span_ms = ev0.elapsed_time(ev1)
     ms_per_step = span_ms / K
-    kern_ms = float(np.mean(per_launch_ms))
+    kern_ms = ms_per_step          # one GEMM launch per step
     del filler
 
     flops = cs.flops
@@ -152,6 +202,12 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[cs.fmt],
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
     roof["kernel"] = mx.mx_variant_name(variant)
+    rec = recorded_traffic(args.workload, roof["kernel"])
+    if rec is not None:
+        roof["traffic"] = rec["hbm_bytes_per_launch"]
+        roof["traffic_unit"] = "bytes/launch"
+        roof["traffic_vs_algorithmic"] = round(rec["hbm_bytes_per_launch"] / alg_bytes, 3)
+    roof["algorithmic_bytes"] = int(alg_bytes)
     roof["kernel_us"] = round(kern_ms * 1e3, 3)
     roof["roofline_us"] = round(max(t_hbm, t_mfma) * 1e6, 3)
 

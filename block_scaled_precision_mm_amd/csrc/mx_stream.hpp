@@ -18,18 +18,21 @@
 //
 // Per wave and group the loads are: for each of the MT A subtiles and WN B
 // subtiles, 4 steps of packed bytes (16 B per lane per step for FP4, 32 B
-// for FP8) and one 16-byte load of the row's 16 scale codes (4 steps x 4
-// blocks).  A ring of D groups lives in registers; the loads of group t+D
-// are issued right after group t's MFMAs, so D groups are in flight.  Each
-// wave starts its run of groups at a rotated position (by workgroup index)
-// so that concurrent waves read A at different addresses instead of all
-// hitting the same L2 channels at once.
+// for FP8), and for each operand one load that gives every lane the 16
+// scale codes (4 steps x 4 blocks) of one row.  The vector-memory address
+// unit, not HBM, limits a kernel that issues many small loads, so the loads
+// are as few as the MFMA layout allows and a ring slot is only refilled
+// with a real group.  A ring of D groups lives in registers; the loads of
+// group t+D are issued right after group t's MFMAs, so D groups are in
+// flight.  Each wave starts its run of groups at a rotated position (by
+// workgroup index) so that concurrent waves read A at different addresses
+// instead of all hitting the same L2 channels at once.
 //
-// Rows past M or N, and ring slots past the end of a wave's run, are read
-// through buffer descriptors whose range excludes them: such loads return
-// zeros without touching memory, and zero codes with zero scale codes add
-// exactly +0 to the accumulators.  The last wave also handles the K steps
-// left over when K/128 is not a multiple of 4.
+// Rows past M or N (and, when a wave has fewer groups than ring slots, the
+// unused slots) are read through buffer descriptors whose range excludes
+// them: such loads return zeros without touching memory, and zero codes
+// with zero scale codes add exactly +0 to the accumulators.  The last wave
+// also handles the K steps left over when K/128 is not a multiple of 4.
 #pragma once
 
 #include "mx_common.hpp"
@@ -48,7 +51,14 @@ struct StreamArgs {
 template <int F, int MT, int WN>
 struct StreamGroup {
     StepFrag<F> a[MT][4], b[WN][4];
-    u4v sa[MT], sb[WN];
+    u4v sca, scb;   // lane L: the group's 16 scale codes of A row L / B row L
+};
+
+// Per-lane offsets of one workgroup's rows.
+template <int MT, int WN>
+struct StreamOffsets {
+    unsigned a[MT], b[WN];   // packed-operand row of lane (r, g) in subtile x / y
+    unsigned sa, sb;         // scale row of lane L (A row L, B row L), or out of range
 };
 
 template <int F, int MT, int WN>
@@ -57,44 +67,45 @@ __device__ __forceinline__ void stream_load_group(StreamGroup<F, MT, WN> &gr,
                                                   __amdgpu_buffer_rsrc_t rb,
                                                   __amdgpu_buffer_rsrc_t rsa,
                                                   __amdgpu_buffer_rsrc_t rsb,
-                                                  const unsigned (&aoff)[MT],
-                                                  const unsigned (&boff)[WN],
-                                                  const unsigned (&asoff)[MT],
-                                                  const unsigned (&bsoff)[WN], int grp, bool valid,
-                                                  int g)
+                                                  const StreamOffsets<MT, WN> &o, int grp,
+                                                  bool valid, int g)
 {
     constexpr unsigned GB = 4 * FmtTraits<F>::step_bytes;   // packed bytes of a group per row
     const unsigned k = valid ? (unsigned)grp * GB : kOutOfRange;
     const unsigned ks = valid ? (unsigned)grp * 16u : kOutOfRange;
+    // scales first, then step by step, so that step 0's MFMAs can start as
+    // soon as the first loads have arrived
+    gr.scb = load16<CPOL_NONE>(rsb, o.sb + ks);
+    gr.sca = load16<CPOL_NONE>(rsa, o.sa + ks);
 #pragma unroll
-    for (int y = 0; y < WN; ++y) {
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            load_step<F, CPOL_NT>(gr.b[y][s], rb, boff[y] + k, s, g);
-        gr.sb[y] = load16<CPOL_NT>(rsb, bsoff[y] + ks);
-    }
+        for (int y = 0; y < WN; ++y)
+            load_step<F, CPOL_NONE>(gr.b[y][s], rb, o.b[y] + k, s, g);
 #pragma unroll
-    for (int x = 0; x < MT; ++x) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            load_step<F, CPOL_NONE>(gr.a[x][s], ra, aoff[x] + k, s, g);
-        gr.sa[x] = load16<CPOL_NONE>(rsa, asoff[x] + ks);
+        for (int x = 0; x < MT; ++x)
+            load_step<F, CPOL_NONE>(gr.a[x][s], ra, o.a[x] + k, s, g);
     }
 }
 
+// The scale codes arrive one row per lane; the MFMA wants row r's code of
+// block g in lane (r, g).  ds_bpermute fetches the row's step dword from the
+// lane that loaded it, and the shift picks the block's byte.
 template <int F, int MT, int WN>
 __device__ __forceinline__ void stream_mfma_group(const StreamGroup<F, MT, WN> &gr,
-                                                  v4f (&acc)[MT][WN], int g)
+                                                  v4f (&acc)[MT][WN], int r, int g)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         unsigned sb[WN], sa[MT];
 #pragma unroll
         for (int y = 0; y < WN; ++y)
-            sb[y] = gr.sb[y][s] >> (8 * g);
+            sb[y] = (unsigned)__builtin_amdgcn_ds_bpermute(4 * (16 * y + r), (int)gr.scb[s]) >>
+                    (8 * g);
 #pragma unroll
         for (int x = 0; x < MT; ++x)
-            sa[x] = gr.sa[x][s] >> (8 * g);
+            sa[x] = (unsigned)__builtin_amdgcn_ds_bpermute(4 * (16 * x + r), (int)gr.sca[s]) >>
+                    (8 * g);
 #pragma unroll
         for (int x = 0; x < MT; ++x)
 #pragma unroll
@@ -109,6 +120,7 @@ template <int F, int MT, int WN, int KW, int D, int OUT>
 __global__ __launch_bounds__(64 * KW)
 void mx_gemm_stream(StreamArgs p)
 {
+    static_assert(MT <= 4 && WN <= 4, "one lane per scale row: at most 64 rows per operand");
     const int lane = threadIdx.x & 63;
     const int kw = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -125,23 +137,26 @@ void mx_gemm_stream(StreamArgs p)
         make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
-    unsigned aoff[MT], asoff[MT], boff[WN], bsoff[WN];
+    StreamOffsets<MT, WN> o;
 #pragma unroll
-    for (int x = 0; x < MT; ++x) {
-        aoff[x] = (unsigned)(16 * x + r) * p.row_bytes;
-        asoff[x] = (unsigned)(16 * x + r) * p.srow_bytes;
-    }
+    for (int x = 0; x < MT; ++x)
+        o.a[x] = (unsigned)(16 * x + r) * p.row_bytes;
 #pragma unroll
-    for (int y = 0; y < WN; ++y) {
-        boff[y] = (unsigned)(16 * y + r) * p.row_bytes;
-        bsoff[y] = (unsigned)(16 * y + r) * p.srow_bytes;
-    }
+    for (int y = 0; y < WN; ++y)
+        o.b[y] = (unsigned)(16 * y + r) * p.row_bytes;
+    o.sa = lane < 16 * MT ? (unsigned)lane * p.srow_bytes : kOutOfRange;
+    o.sb = lane < 16 * WN ? (unsigned)lane * p.srow_bytes : kOutOfRange;
 
     // This wave's run of groups, [g0, g0 + ng), visited from a rotated start.
     const int ngroups = p.nsteps >> 2;
     const int g0 = (int)(((long long)kw * ngroups) / KW);
     const int ng = (int)(((long long)(kw + 1) * ngroups) / KW) - g0;
     const int phase = ng > 0 ? (int)((blockIdx.x + 3u * blockIdx.y) % (unsigned)ng) : 0;
+    auto group_at = [&](int t) {
+        int idx = t + phase;
+        if (idx >= ng) idx -= ng;
+        return g0 + idx;
+    };
 
     v4f acc[MT][WN];
 #pragma unroll
@@ -150,29 +165,42 @@ void mx_gemm_stream(StreamArgs p)
         for (int y = 0; y < WN; ++y)
             acc[x][y] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Ring prologue: D groups, issued unconditionally (slots past the run
+    // read zeros) so that the wait counts of every later MFMA are exact.
     StreamGroup<F, MT, WN> ring[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-        int idx = i + phase;
-        if (idx >= ng) idx -= ng;
-        stream_load_group<F, MT, WN>(ring[i], ra, rb, rsa, rsb, aoff, boff, asoff, bsoff, g0 + idx,
-                                     i < ng, g);
+        stream_load_group<F, MT, WN>(ring[i], ra, rb, rsa, rsb, o, group_at(i), i < ng, g);
         // keep the slots' loads in ring order: the wait counts at the MFMAs
         // rely on slot i being issued before slot i+1
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int t = 0; t < ng; t += D) {
+    // Steady state: every refill is a real group.
+    int t = 0;
+    for (; t + 2 * D <= ng; t += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            stream_mfma_group<F, MT, WN>(ring[i], acc, g);
-            const int nt = t + i + D;
-            int idx = nt + phase;
-            if (idx >= ng) idx -= ng;
-            stream_load_group<F, MT, WN>(ring[i], ra, rb, rsa, rsb, aoff, boff, asoff, bsoff,
-                                         g0 + idx, nt < ng, g);
+            stream_mfma_group<F, MT, WN>(ring[i], acc, r, g);
+            stream_load_group<F, MT, WN>(ring[i], ra, rb, rsa, rsb, o, group_at(t + D + i), true,
+                                         g);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // Drain: the slots hold groups t .. t+D-1 (those that exist); fewer than
+    // D more remain to be loaded.
+    const int rem = ng - t;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        if (i < rem)
+            stream_mfma_group<F, MT, WN>(ring[i], acc, r, g);
+        if (D + i < rem)
+            stream_load_group<F, MT, WN>(ring[i], ra, rb, rsa, rsb, o, group_at(t + D + i), true,
+                                         g);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (D + i < rem)
+            stream_mfma_group<F, MT, WN>(ring[i], acc, r, g);
 
     // K steps beyond the last whole group (K/128 not a multiple of 4).
     const int tail = p.nsteps & 3;
@@ -182,13 +210,13 @@ void mx_gemm_stream(StreamArgs p)
             unsigned sa[MT], sb[WN];
 #pragma unroll
             for (int y = 0; y < WN; ++y) {
-                load_step<F, CPOL_NT>(fb[y], rb, boff[y], s, g);
-                sb[y] = load4(rsb, bsoff[y] + 4u * s) >> (8 * g);
+                load_step<F, CPOL_NONE>(fb[y], rb, o.b[y], s, g);
+                sb[y] = load4(rsb, (unsigned)(16 * y + r) * p.srow_bytes + 4u * s) >> (8 * g);
             }
 #pragma unroll
             for (int x = 0; x < MT; ++x) {
-                load_step<F, CPOL_NONE>(fa[x], ra, aoff[x], s, g);
-                sa[x] = load4(rsa, asoff[x] + 4u * s) >> (8 * g);
+                load_step<F, CPOL_NONE>(fa[x], ra, o.a[x], s, g);
+                sa[x] = load4(rsa, (unsigned)(16 * x + r) * p.srow_bytes + 4u * s) >> (8 * g);
             }
 #pragma unroll
             for (int x = 0; x < MT; ++x)
@@ -224,13 +252,13 @@ void mx_gemm_stream(StreamArgs p)
         constexpr int NQ = 16 * MT * 4 * WN;   // float4 column groups in the tile
         for (int q = threadIdx.x; q < NQ; q += 64 * KW) {
             const int row = q / (4 * WN), c4 = q % (4 * WN);
-            v4f s = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
+            v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
 #pragma unroll
             for (int w = 1; w < KW; ++w)
-                s += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
+                sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
             const int m = m0 + row, n = n0 + 4 * c4;
             if (m < p.M && n < p.N)
-                store4<OUT>(p.c, p.N, m, n, s, vec_ok && n + 3 < p.N);
+                store4<OUT>(p.c, p.N, m, n, sum, vec_ok && n + 3 < p.N);
         }
     }
 }

@@ -134,13 +134,14 @@ int find_variant(int mt, int wn, int kw)
 // units.
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
+    (void)is_fp4;
     (void)K;
     if (M <= 16)
-        return find_variant(1, N >= 256 * 64 ? 4 : (N >= 256 * 32 ? 2 : 1), 4);
+        return find_variant(1, N >= 8192 ? 2 : 1, 4);
     if (M <= 32)
-        return find_variant(2, N >= 256 * 32 ? 2 : 1, 4);
+        return N >= 8192 ? find_variant(2, 4, 8) : find_variant(2, 1, 4);
     if (M <= 64)
-        return is_fp4 ? find_variant(2, 2, 8) : find_variant(2, 2, 8);
+        return find_variant(2, 2, 4);
     return find_variant(4, 4, 4);
 }
 
