@@ -45,6 +45,8 @@ _lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P
 _lib.mx_scaled_mm_fp8.argtypes = _lib.mx_scaled_mm_fp4.argtypes
 _lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
 _lib.mx_default_variant.argtypes = [_INT, _I64, _I64, _I64]
+_lib.mx_variant_max_k.argtypes = [_INT, _INT]
+_lib.mx_variant_max_k.restype = _I64
 _lib.mx_status_string.argtypes = [_INT]
 _lib.mx_status_string.restype = ctypes.c_char_p
 _lib.mx_variant_name.argtypes = [_INT]
@@ -55,8 +57,8 @@ for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
 
 # every symbol include/mxgemm.h declares
 EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
-           "mx_variant_name", "mx_default_variant", "mx_status_string", "mx_last_hip_error",
-           "mx_abi_version")
+           "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
+           "mx_last_hip_error", "mx_abi_version")
 
 
 class MxGemmError(RuntimeError):
@@ -141,6 +143,18 @@ def mx_default_variant(is_fp4, M, N, K) -> int:
 
 def mx_num_variants() -> int:
     return int(_lib.mx_num_variants())
+
+
+def mx_variant_max_k(variant, is_fp4) -> int:
+    v = int(_lib.mx_variant_max_k(variant, int(bool(is_fp4))))
+    if v < 0:
+        raise MxGemmError(v, "mx_variant_max_k")
+    return v
+
+
+def variants_for(is_fp4, K):
+    """Every variant that accepts this format and K."""
+    return [v for v in range(mx_num_variants()) if K <= mx_variant_max_k(v, is_fp4)]
 
 
 def mx_variant_name(variant) -> str | None:

@@ -60,6 +60,16 @@ template <> struct FmtTraits<FMT_FP4> {
     static constexpr int mfma_code = 4;     // instruction format code for E2M1
 };
 
+// Kernel arguments shared by every kernel family.
+struct GemmArgs {
+    const uint8_t *a, *b, *sa, *sb;
+    void *c;
+    int M, N;
+    int nsteps;           // K / 128
+    unsigned row_bytes;   // packed bytes per operand row: K/2 (FP4) or K (FP8)
+    unsigned srow_bytes;  // scale bytes per row: K/32
+};
+
 // Cache-policy bits of a buffer load on gfx950: 2 = non-temporal (stream).
 enum { CPOL_NONE = 0, CPOL_NT = 2 };
 

@@ -39,15 +39,6 @@
 
 namespace mxg {
 
-struct StreamArgs {
-    const uint8_t *a, *b, *sa, *sb;
-    void *c;
-    int M, N;
-    int nsteps;           // K / 128
-    unsigned row_bytes;   // packed bytes per operand row: K/2 (FP4) or K (FP8)
-    unsigned srow_bytes;  // scale bytes per row: K/32
-};
-
 template <int F, int MT, int WN>
 struct StreamGroup {
     StepFrag<F> a[MT][4], b[WN][4];
@@ -118,11 +109,11 @@ __device__ __forceinline__ void stream_mfma_group(const StreamGroup<F, MT, WN> &
 // flight per wave.
 template <int F, int MT, int WN, int KW, int D, int OUT>
 __global__ __launch_bounds__(64 * KW)
-void mx_gemm_stream(StreamArgs p)
+void mx_gemm_stream(GemmArgs p)
 {
     static_assert(MT <= 4 && WN <= 4, "one lane per scale row: at most 64 rows per operand");
     const int lane = threadIdx.x & 63;
-    const int kw = threadIdx.x >> 6;
+    const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
     const int m0 = blockIdx.y * (16 * MT);
     const int n0 = blockIdx.x * (16 * WN);

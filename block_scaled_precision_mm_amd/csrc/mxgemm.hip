@@ -15,6 +15,8 @@
 #include <atomic>
 
 #include "../../include/mxgemm.h"
+#include "mx_decode.hpp"
+#include "mx_lds.hpp"
 #include "mx_stream.hpp"
 
 using namespace mxg;
@@ -24,16 +26,19 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 // ------------------------------------------------------------------ variants
-typedef void (*StreamFn)(StreamArgs);
+typedef void (*KernelFn)(GemmArgs);
 
 struct Variant {
     const char *name;
-    int mt, wn, kw;          // 16*mt x 16*wn output tile, kw waves splitting K
-    StreamFn fn[2][3];       // [fmt][out]
+    int bm, bn;              // workgroup output tile
+    int threads;
+    KernelFn fn[2][3];       // [fmt][out]
+    int kmax[2];             // largest K per format (0: any K)
 };
 
-// Ring depth (groups in flight per wave) from a register budget: a ring slot
-// holds 4 steps of every A and B subtile plus their scale codes.
+// Ring depth of the register-streaming kernel (groups in flight per wave)
+// from a register budget: a ring slot holds 4 steps of every A and B
+// subtile plus their scale codes.
 constexpr int ring_depth(int fmt, int mt, int wn)
 {
     return (mt + wn) * (fmt == FMT_FP4 ? 20 : 36) <= 80 ? 2 : 1;
@@ -42,8 +47,30 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 #define MXG_SFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O>)
 #define MXG_SOUTS(F, MT, WN, KW) \
     {MXG_SFN(F, MT, WN, KW, OUT_BF16), MXG_SFN(F, MT, WN, KW, OUT_F16), MXG_SFN(F, MT, WN, KW, OUT_F32)}
-#define MXG_STREAM(MT, WN, KW) \
-    {"stream_" #MT "x" #WN "_k" #KW, MT, WN, KW, {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}}
+#define MXG_STREAM(MT, WN, KW)                                                        \
+    {"stream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                        \
+     {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}}
+
+// LDS-staged kernel: KW K groups of WM x WN waves with MT x NT subtiles each;
+// S4 / S8 steps per stage and T4 / T8 stages for FP4 / FP8.
+#define MXG_LFN(F, KW, WM, WN, MT, NT, S, ST, O) (&mx_gemm_lds<F, KW, WM, WN, MT, NT, S, ST, O>)
+#define MXG_LOUTS(F, KW, WM, WN, MT, NT, S, ST)                                        \
+    {MXG_LFN(F, KW, WM, WN, MT, NT, S, ST, OUT_BF16), MXG_LFN(F, KW, WM, WN, MT, NT, S, ST, OUT_F16), \
+     MXG_LFN(F, KW, WM, WN, MT, NT, S, ST, OUT_F32)}
+#define MXG_LDS(NAME, KW, WM, WN, MT, NT, S4, S8, T4, T8)                             \
+    {NAME, 16 * MT * WM, 16 * NT * WN, 64 * KW * WM * WN,                             \
+     {MXG_LOUTS(FMT_FP8, KW, WM, WN, MT, NT, S8, T8), MXG_LOUTS(FMT_FP4, KW, WM, WN, MT, NT, S4, T4)}, {0, 0}}
+
+// Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
+// (K up to K8 / K4 for FP8 / FP4), NW waves of NT B subtiles each streaming
+// through private rings of D stages of S8 / S4 steps.
+#define MXG_DFN(F, MT, NW, NT, S, D, KM, O) (&mx_gemm_decode<F, MT, NW, NT, S, D, KM, O>)
+#define MXG_DOUTS(F, MT, NW, NT, S, D, KM)                                                  \
+    {MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_BF16), MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_F16),  \
+     MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_F32)}
+#define MXG_DECODE(NAME, MT, NW, NT, S4, S8, D, K4, K8)                                    \
+    {NAME, 16 * MT, 16 * NT * NW, 64 * NW,                                                 \
+     {MXG_DOUTS(FMT_FP8, MT, NW, NT, S8, D, K8), MXG_DOUTS(FMT_FP4, MT, NW, NT, S4, D, K4)}, {K8, K4}}
 
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
@@ -58,13 +85,26 @@ const Variant kVariants[] = {
     MXG_STREAM(4, 1, 8),
     MXG_STREAM(4, 2, 8),
     MXG_STREAM(4, 4, 4),
+    //       name                 KW WM WN MT NT S4 S8 T4 T8
+    MXG_LDS("lds_16x64_w4",        1, 1, 4, 1, 1, 4, 2, 4, 4),
+    MXG_LDS("lds_32x64_w4",        1, 1, 4, 2, 1, 4, 2, 4, 4),
+    MXG_LDS("lds_64x16_k4",        4, 1, 1, 4, 1, 2, 1, 3, 3),
+    MXG_LDS("lds_32x32_k4",        4, 1, 1, 2, 2, 2, 1, 3, 3),
+    MXG_LDS("lds_64x64_w2x2",      1, 2, 2, 2, 2, 4, 2, 3, 3),
+    MXG_LDS("lds_128x128_w2x2",    1, 2, 2, 4, 4, 2, 1, 3, 3),
+    MXG_LDS("lds_256x128_w2x2",    1, 2, 2, 8, 4, 1, 1, 3, 3),
+    MXG_LDS("lds_256x256_w2x2",    1, 2, 2, 8, 8, 1, 1, 3, 2),
+    //          name              MT NW NT S4 S8 D  K4    K8
+    MXG_DECODE("decode_32x64",    2, 4, 1, 4, 2, 5, 4096, 2048),
+    MXG_DECODE("decode_16x64",    1, 4, 1, 4, 2, 6, 4096, 2048),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 // ---------------------------------------------------------------- validation
-// Largest K: every per-workgroup buffer range (at most 64 rows) must stay
+// Largest K: every per-workgroup buffer range (at most 256 rows) must stay
 // below 2^31 bytes.
 constexpr int64_t kMaxK = (int64_t)1 << 22;
+static_assert(256 * kMaxK < ((int64_t)1 << 31), "per-workgroup buffer range");
 
 int validate(const void *a, const void *b, const void *sa, const void *sb, const void *c,
              int64_t M, int64_t N, int64_t K, int out_dtype)
@@ -120,10 +160,10 @@ int check_device()
 // ------------------------------------------------------------ configuration
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int find_variant(int mt, int wn, int kw)
+int find_variant(const char *name)
 {
     for (int i = 0; i < kNumVariants; ++i)
-        if (kVariants[i].mt == mt && kVariants[i].wn == wn && kVariants[i].kw == kw)
+        if (strcmp(kVariants[i].name, name) == 0)
             return i;
     return 0;
 }
@@ -137,19 +177,22 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     (void)is_fp4;
     (void)K;
     if (M <= 16)
-        return find_variant(1, N >= 8192 ? 2 : 1, 4);
+        return find_variant(N >= 8192 ? "stream_1x2_k4" : "stream_1x1_k4");
     if (M <= 32)
-        return N >= 8192 ? find_variant(2, 4, 8) : find_variant(2, 1, 4);
+        return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
     if (M <= 64)
-        return find_variant(2, 2, 4);
-    return find_variant(4, 4, 4);
+        return find_variant("stream_2x2_k4");
+    return find_variant("stream_4x4_k4");
 }
 
 int launch(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
            int64_t M, int64_t N, int64_t K, int out_dtype, int variant, hipStream_t stream)
 {
     const Variant &v = kVariants[variant];
-    StreamArgs p;
+    const int kmax = v.kmax[is_fp4 ? 1 : 0];
+    if (kmax && K > kmax)
+        return MXG_ERR_CONFIG;
+    GemmArgs p;
     p.a = (const uint8_t *)a;
     p.b = (const uint8_t *)b;
     p.sa = (const uint8_t *)sa;
@@ -160,11 +203,11 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     p.nsteps = (int)(K / 128);
     p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
     p.srow_bytes = (unsigned)(K / 32);
-    const int64_t gx = cdiv(N, 16 * v.wn), gy = cdiv(M, 16 * v.mt);
+    const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
     if (gx > INT32_MAX || gy > 65535)
         return MXG_ERR_SHAPE;
-    StreamFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype];
-    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(64 * v.kw), 0, stream, p);
+    KernelFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype];
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(v.threads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
@@ -220,6 +263,9 @@ int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_
         return rc;
     if (variant < 0 || variant >= kNumVariants)
         return MXG_ERR_CONFIG;
+    const int kmax = kVariants[variant].kmax[is_fp4 ? 1 : 0];
+    if (kmax && K > kmax)
+        return MXG_ERR_CONFIG;
     rc = check_device();
     if (rc)
         return rc;
@@ -228,6 +274,14 @@ int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_
 }
 
 int mx_num_variants(void) { return kNumVariants; }
+
+int64_t mx_variant_max_k(int variant, int is_fp4)
+{
+    if (variant < 0 || variant >= kNumVariants)
+        return MXG_ERR_CONFIG;
+    const int km = kVariants[variant].kmax[is_fp4 ? 1 : 0];
+    return km ? km : kMaxK;
+}
 
 const char *mx_variant_name(int variant)
 {

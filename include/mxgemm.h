@@ -99,12 +99,17 @@ int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const vo
  * (0 .. mx_num_variants()-1) instead of the one the default entry points
  * pick.  is_fp4: 1 for MXFP4 operands, 0 for MXFP8.  Same operand contract
  * and errors as mx_scaled_mm_fp4/fp8, plus MXG_ERR_CONFIG for an unknown
- * variant.  Every variant computes the same product; they differ in tiling
+ * variant or a K beyond the variant's limit (mx_variant_max_k).  Every variant computes the same product; they differ in tiling
  * and therefore in FP32 accumulation order. */
 int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
                         int out_dtype, int variant, mxg_stream_t stream);
 int mx_num_variants(void);
+/* Largest K a variant accepts for the format (is_fp4: 1 MXFP4, 0 MXFP8);
+ * some variants keep the whole A tile in LDS and so bound K.  Returns
+ * MXG_ERR_CONFIG for an unknown variant.  A call with a larger K returns
+ * MXG_ERR_CONFIG. */
+int64_t mx_variant_max_k(int variant, int is_fp4);
 /* Human-readable name of a variant (tile shape), or NULL if out of range. */
 const char *mx_variant_name(int variant);
 

@@ -34,6 +34,8 @@ def lib():
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_variant_name.restype = ctypes.c_char_p
     L.mx_default_variant.argtypes = [INT, I64, I64, I64]
+    L.mx_variant_max_k.argtypes = [INT, INT]
+    L.mx_variant_max_k.restype = I64
     return L
 
 
@@ -100,6 +102,16 @@ def test_invalid_configs(lib):
     ok = (A, A, A, A, A, 64, 64, 512, 0)
     assert lib.mx_scaled_mm_config(1, *ok, -1, None) == -9
     assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), None) == -9
+    # a variant that keeps A resident in LDS rejects K beyond its capacity
+    for v in range(lib.mx_num_variants()):
+        for is4 in (0, 1):
+            kmax = lib.mx_variant_max_k(v, is4)
+            assert kmax >= 512 and kmax % 128 == 0
+            if kmax < (1 << 22):
+                args = (A, A, A, A, A, 64, 64, kmax + 128, 0)
+                assert lib.mx_scaled_mm_config(is4, *args, v, None) == -9
+    assert lib.mx_variant_max_k(-1, 1) == -9
+    assert lib.mx_variant_max_k(lib.mx_num_variants(), 0) == -9
     # argument errors take precedence over the variant check
     assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 64, 64, 500, 0, 0, None) == -3
     assert lib.mx_scaled_mm_config(0, 0, A, A, A, A, 64, 64, 512, 0, 0, None) == -1

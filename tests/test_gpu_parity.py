@@ -88,7 +88,7 @@ def test_small_shapes_every_variant(mx, fmt, shape):
     M, N, K = shape
     a, b, sa, sb = quantized(fmt, M, N, K, seed=M * 131 + N * 7 + K)
     print("case", fmt, shape, flush=True)
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(fmt == "fp4", K):
         full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v,
                    what="%s %s %s" % (fmt, shape, mx.mx_variant_name(v)))
 
@@ -129,7 +129,7 @@ def test_fp4_all_code_pairs_exact(mx, pos):
     A, B, sa, sb = _one_hot("fp4", codes, codes, K, pos)
     # a sum that starts from +0 is +0 when every term is a zero (+0 + -0 = +0)
     exact = np.outer(refdecode.e2m1(codes), refdecode.e2m1(codes)) + 0.0
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(True, K):
         c32 = run(mx, "fp4", A, B, sa, sb, 16, 16, K, "f32", variant=v)
         assert np.array_equal(c32, exact), "variant %d pos %d" % (v, pos)
         bits = run(mx, "fp4", A, B, sa, sb, 16, 16, K, "bf16", variant=v)
@@ -143,7 +143,7 @@ def test_fp8_all_code_pairs_exact(mx, pos):
     A, B, sa, sb = _one_hot("fp8", codes, codes, K, pos)
     va = refdecode.e4m3(codes)
     exact = np.outer(va, va) + 0.0                 # NaN rows/cols for the two NaN codes; -0 -> +0
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(False, K):
         c32 = run(mx, "fp8", A, B, sa, sb, 256, 256, K, "f32", variant=v)
         nan = np.isnan(exact)
         assert np.array_equal(np.isnan(c32), nan)
@@ -162,7 +162,7 @@ def test_fp4_integer_valued_exact(mx):
     Ai = (refdecode.values("fp4", a, M, K) * 2).astype(np.int64)
     Bi = (refdecode.values("fp4", b, N, K) * 2).astype(np.int64)
     exact = (Ai @ Bi.T).astype(np.float64)
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(True, K):
         assert np.array_equal(run(mx, "fp4", a, b, sa, sb, M, N, K, "f32", v), exact)
 
 
@@ -181,7 +181,7 @@ def test_fp8_integer_valued_exact(mx):
     sb = np.full((N, K // 32), 127, np.uint8)
     exact = (refdecode.values("fp8", a, M, K).astype(np.int64) @
              refdecode.values("fp8", b, N, K).astype(np.int64).T).astype(np.float64)
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(False, K):
         assert np.array_equal(run(mx, "fp8", a, b, sa, sb, M, N, K, "f32", v), exact)
 
 
@@ -206,7 +206,7 @@ def test_nan_scale_and_nan_code(mx, fmt):
     if fmt == "fp8":
         b[12, 99] = 0x7F
     cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(fmt == "fp4", K):
         c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
         assert np.array_equal(np.isnan(c32), np.isnan(cref)), "variant %d" % v
         for kind in ("bf16", "f16"):
@@ -221,7 +221,7 @@ def test_deterministic(mx):
     r1 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
     r2 = run(mx, fmt, a, b, sa, sb, M, N, K, "bf16")
     assert np.array_equal(r1, r2)
-    for v in range(mx.mx_num_variants()):
+    for v in mx.variants_for(fmt == "fp4", K):
         x1 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
         x2 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
         assert np.array_equal(x1, x2), "%s not deterministic" % mx.mx_variant_name(v)
