@@ -18,6 +18,7 @@
 #include "mx_decode.hpp"
 #include "mx_lds.hpp"
 #include "mx_stream.hpp"
+#include "mx_tile.hpp"
 
 using namespace mxg;
 
@@ -34,6 +35,7 @@ struct Variant {
     int threads;
     KernelFn fn[2][3];       // [fmt][out]
     int kmax[2];             // largest K per format (0: any K)
+    int linear;              // 1: one-dimensional grid, the kernel maps blocks to tiles
 };
 
 // Ring depth of the register-streaming kernel (groups in flight per wave)
@@ -72,6 +74,14 @@ constexpr int ring_depth(int fmt, int mt, int wn)
     {NAME, 16 * MT, 16 * NT * NW, 64 * NW,                                                 \
      {MXG_DOUTS(FMT_FP8, MT, NW, NT, S8, D, K8), MXG_DOUTS(FMT_FP4, MT, NW, NT, S4, D, K4)}, {K8, K4}}
 
+// Large tiles on the 32x32x64 instruction, staged through registers.
+#define MXG_TFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O>)
+#define MXG_TOUTS(F, MT, NT) \
+    {MXG_TFN(F, MT, NT, OUT_BF16), MXG_TFN(F, MT, NT, OUT_F16), MXG_TFN(F, MT, NT, OUT_F32)}
+#define MXG_TILE(NAME, MT, NT)                                                      \
+    {NAME, 64 * (MT), 64 * (NT), 256,                                               \
+     {MXG_TOUTS(FMT_FP8, MT, NT), MXG_TOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1}
+
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
     MXG_STREAM(1, 2, 4),
@@ -97,6 +107,11 @@ const Variant kVariants[] = {
     //          name              MT NW NT S4 S8 D  K4    K8
     MXG_DECODE("decode_32x64",    2, 4, 1, 4, 2, 5, 4096, 2048),
     MXG_DECODE("decode_16x64",    1, 4, 1, 4, 2, 6, 4096, 2048),
+
+    MXG_TILE("tile_256x256",      4, 4),
+    MXG_TILE("tile_256x128",      4, 2),
+    MXG_TILE("tile_128x256",      2, 4),
+    MXG_TILE("tile_128x128",      2, 2),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -168,10 +183,11 @@ int find_variant(const char *name)
     return 0;
 }
 
-// Default tile choice.  The output tile should be as square as the row
-// count allows (per-CU traffic is proportional to tile rows + tile
-// columns), and there should be at least as many workgroups as compute
-// units.
+// Default tile choice, from measured sweeps on MI355X.  Up to 64 rows of A
+// the product is a B stream and the register-streaming kernel wins; beyond
+// that the register-staged tile kernels take over, with the largest tile
+// that still gives every compute unit work (per-CU traffic is proportional
+// to tile rows + tile columns, so bigger tiles move fewer bytes per FLOP).
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     (void)is_fp4;
@@ -182,7 +198,11 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
     if (M <= 64)
         return find_variant("stream_2x2_k4");
-    return find_variant("stream_4x4_k4");
+    if (cdiv(M, 256) * cdiv(N, 256) >= 384)
+        return find_variant("tile_256x256");
+    if (cdiv(M, 256) * cdiv(N, 128) >= 192)
+        return find_variant("tile_256x128");
+    return find_variant("tile_128x128");
 }
 
 int launch(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
@@ -204,10 +224,18 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
     p.srow_bytes = (unsigned)(K / 32);
     const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
-    if (gx > INT32_MAX || gy > 65535)
-        return MXG_ERR_SHAPE;
+    dim3 grid;
+    if (v.linear) {
+        if (gx * gy > INT32_MAX)
+            return MXG_ERR_SHAPE;
+        grid = dim3((unsigned)(gx * gy));
+    } else {
+        if (gx > INT32_MAX || gy > 65535)
+            return MXG_ERR_SHAPE;
+        grid = dim3((unsigned)gx, (unsigned)gy);
+    }
     KernelFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype];
-    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(v.threads), 0, stream, p);
+    hipLaunchKernelGGL(fn, grid, dim3(v.threads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;

@@ -79,7 +79,11 @@ def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, what=""):
 # waves), 5 and 9 (a group run plus a leftover step), 12, 16 (several groups
 # per wave); M and N ragged against every tile size
 SMALL_SHAPES = [(1, 1, 128), (5, 17, 256), (257, 129, 384), (16, 64, 512), (33, 200, 640),
-                (100, 130, 1152), (70, 47, 1536), (3, 1000, 2048)]
+                (100, 130, 1152), (70, 47, 1536), (3, 1000, 2048),
+                # several 256-row tiles with ragged tails; a grid of exactly 8
+                # large tiles (the tile-order remap applies when the count is a
+                # multiple of 8)
+                (600, 520, 1024), (512, 1024, 256)]
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
