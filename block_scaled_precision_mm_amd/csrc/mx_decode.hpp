@@ -1,249 +1,238 @@
-// mx_decode.hpp -- NT MX block-scaled GEMM for decode-width products
-// (a few dozen rows of A), gfx950.
+// mx_decode.hpp -- NT MX block-scaled GEMM for decode-width products (up to
+// 32 rows of A), gfx950.
 //
-// At small M every byte of B is used by one workgroup only and the product
-// is bound by how fast B streams from HBM.  Measured on MI355X, a workgroup
-// that shares its B stages through LDS pays a barrier and an LDS round trip
-// per stage, and re-loading the A and scale tiles with every stage adds
-// about half as many L1 requests again as B itself.  This kernel instead:
+// At small M every byte of B is used once: the product is a B stream, and
+// the MFMA work is a few percent of the time.  Measured on MI355X, what
+// sets the stream's speed is the shape of the loads:
+//   * DRAM: B rows read in long contiguous runs by one wave stream faster
+//     than the same rows cut into 64-byte slices read by different waves
+//     (split-K), and reading A once per workgroup instead of once per wave
+//     saves its share of the traffic;
+//   * L1: a 16-byte-per-lane load whose lanes follow the MFMA operand layout
+//     (16 rows in consecutive lanes) costs ~2.5x the address cycles of a
+//     coalesced one, and a one-row-per-lane scale load ~4x.
+// So:
+//   * a workgroup of NW waves owns 16*NW consecutive B rows and all 16*MT A
+//     rows; wave w streams B rows [16w, 16w+16) over the whole of K -- no
+//     split-K, no reduction, no barrier in the K loop;
+//   * the A tile and the scale codes of all the workgroup's rows are loaded
+//     once, as flat coalesced ranges, into LDS (hence the K limit KMAX: the
+//     A tile must fit);
+//   * B stages of 256 bytes per row are loaded with 16-byte loads in which
+//     16 consecutive lanes read one row's 256 contiguous bytes, into a
+//     G-deep register ring, stored into one of two private LDS slots and
+//     read back as 16x16x128 MFMA fragments.
 //
-//   * loads the whole A tile (16*MT rows x K) and the scale codes of all its
-//     A and B rows into LDS once, at the start (one barrier);
-//   * gives every wave its own B rows (16*WN of them) and its own ring of D
-//     stages in LDS, filled with coalesced direct-to-LDS loads (four
-//     consecutive lanes per 64-byte segment) and consumed by the same wave,
-//     so the K loop has no barrier at all: a wave only waits for its own
-//     loads (s_waitcnt vmcnt);
-//   * reads MFMA fragments with ds_read_b128 from XOR-swizzled rows (chunk
-//     index ^ row % 16), so the 16 rows of one read fall on different banks.
+// LDS layouts: code rows in groups of 8, chunk-major inside a group (chunk c
+// of the 8 rows = 128 contiguous bytes) with a padded chunk stride of 160
+// bytes, so both the fragment reads and the staging stores run at full LDS
+// rate; scale codes as [128-K step][row] dwords, so a step's codes of 16
+// consecutive rows are contiguous.
 //
-// The workgroup's output tile is 16*MT x 16*WN*NW; every wave covers all of
-// K for its 16*WN columns.  The host picks this kernel only when the
-// resident A tile and scale codes fit next to the rings (K <= KMAX).
-//
-// Ragged M / N and the K tail use offsets outside the buffer range: such a
-// direct-to-LDS load writes zeros and moves no data.  Every LDS byte the
-// kernel reads is written this way or by a real load -- the resident rows
-// are loaded over their full KMAX-based stride.  Ragged rows meet zero codes
-// and add exactly +0; steps past K in the last stage are skipped.
+// Ragged M / N: rows past the operand read as zeros (out of the buffer
+// range) and add exactly +0.  K tail: a B stage that runs past the row end
+// reads the next row's bytes, so MFMA steps past K are skipped.
 #pragma once
 
-#include <type_traits>
-
 #include "mx_lds.hpp"
+#include "mx_tile.hpp"
 
 namespace mxg {
 
-template <int F, int MT, int NW, int WN, int SPS, int D, int KMAX>
+template <int F, int MT, int NW, int KMAX>
 struct DecodeGeom {
-    static constexpr int SB = FmtTraits<F>::step_bytes;     // bytes per row per step
-    static constexpr int BM = 16 * MT;
-    static constexpr int BNW = 16 * WN;                      // B rows per wave
-    static constexpr int BN = BNW * NW;
-    static constexpr int RS = KMAX / 128 * SB;               // resident A row stride (bytes)
-    static constexpr int SRS = KMAX / 32;                    // resident scale row stride (bytes)
-    static constexpr int W = SPS * SB;                       // ring row bytes per stage
-    static constexpr int CPR = W / 16;
-    static constexpr int RPB = 1024 / W;                     // ring rows per 1 KB block
-    static constexpr int LPS = BNW * W / 1024;               // ring loads per stage per wave
-    // LDS layout
-    static constexpr int A_OFF = 0;
-    static constexpr int SA_OFF = A_OFF + BM * RS;
-    static constexpr int SB_OFF = SA_OFF + BM * SRS;
-    static constexpr int PAD_OFF = SB_OFF + BN * SRS;          // target of padding loads
-    static constexpr int RING_OFF = (PAD_OFF + 256 + 1023) / 1024 * 1024;
-    static constexpr int SLOT = BNW * W;                     // one stage of one wave
-    static constexpr int BYTES = RING_OFF + NW * D * SLOT;
-    // resident jobs (1 KB each), spread over the NW waves
-    static constexpr int AJOBS = BM * RS / 1024;
-    static constexpr int SJOBS = (BM + BN) * SRS / 1024;
-    static constexpr int RJOBS = AJOBS + SJOBS;
-    static constexpr int RPW = cdiv_c(RJOBS, NW);            // resident loads per wave
-    static_assert(RS % 1024 == 0 && BM * SRS % 1024 == 0 && BN * SRS % 1024 == 0,
-                  "resident rows in whole blocks, A and B scale rows in separate blocks");
-    static_assert(RS / 16 >= 16, "row swizzle needs 16 chunks per resident row");
-    static_assert(W <= 1024 && CPR >= 4 && BNW % RPB == 0, "ring stage must be whole blocks");
+    static constexpr int SB = FmtTraits<F>::step_bytes;      // bytes per row per 128-K step
+    static constexpr int BM = 16 * MT;                       // A rows
+    static constexpr int BN = 16 * NW;                       // B rows (16 per wave)
+    static constexpr int CHUNK = 160;                        // padded 16-byte chunk stride
+    static constexpr int SW = 256;                           // B stage: bytes per row
+    static constexpr int SPS = SW / SB;                      // MFMA steps per stage
+    static constexpr int SCH = SW / 16;                      // chunks per row per stage
+    static constexpr int SLOT = 2 * SCH * CHUNK;             // 16 rows = 2 groups of 8
+    static constexpr int RB_MAX = KMAX / 128 * SB;           // A row bytes at K = KMAX
+    static constexpr int ACH = RB_MAX / 16;                  // A chunks per row at KMAX
+    static constexpr int AGROUP = ACH * CHUNK;               // one 8-row group of A
+    static constexpr int NSTEP_MAX = KMAX / 128;
+    // LDS map
+    static constexpr int SA_OFF = BM / 8 * AGROUP;                         // [step][BM] dwords
+    static constexpr int SBS_OFF = SA_OFF + NSTEP_MAX * BM * 4;            // [step][BN] dwords
+    static constexpr int B_OFF = SBS_OFF + NSTEP_MAX * BN * 4;             // [wave][2] slots
+    static constexpr int BYTES = B_OFF + NW * 2 * SLOT;
+    // coalesced prologue loads per wave: A chunks (16 bytes), scale dwords
+    static constexpr int PA = cdiv_c(BM * ACH, 64 * NW);
+    static constexpr int PS = cdiv_c((BM + BN) * NSTEP_MAX, 64 * NW);
+    static_assert(BM % 8 == 0 && SW % SB == 0 && KMAX % 512 == 0, "tile geometry");
     static_assert(BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
-    static_assert((D - 2) * LPS + RPW < 64, "outstanding loads must fit the vmcnt field");
-    // ring row swizzle (rows of one wave's stage): as in the LDS kernel
-    static constexpr int ROWS_PER_256 = W >= 256 ? 1 : 256 / W;
-    static constexpr int SWZ_MASK = (CPR < 16 ? CPR : 16) - 1;
-    __device__ static constexpr int ring_off(int row, int c)
+    __device__ static constexpr int a_off(int row, int c)
     {
-        return (row / RPB) * 1024 + (row % RPB) * W + 16 * (c ^ ((row / ROWS_PER_256) & SWZ_MASK));
+        return (row >> 3) * AGROUP + c * CHUNK + (row & 7) * 16;
     }
-    __device__ static constexpr int a_off(int row, int c) { return row * RS + 16 * (c ^ (row & 15)); }
+    __device__ static constexpr int b_off(int row, int c)   // within a wave's slot
+    {
+        return (row >> 3) * (SCH * CHUNK) + c * CHUNK + (row & 7) * 16;
+    }
 };
 
-template <int LPS, int D>
-__device__ __forceinline__ void decode_wait(int later)
-{
-    static_assert(D >= 2 && D <= 8, "ring depth");
-    if constexpr (D >= 8) { if (later >= 6) { wait_vm<6 * LPS>(); return; } }
-    if constexpr (D >= 7) { if (later >= 5) { wait_vm<5 * LPS>(); return; } }
-    if constexpr (D >= 6) { if (later >= 4) { wait_vm<4 * LPS>(); return; } }
-    if constexpr (D >= 5) { if (later >= 3) { wait_vm<3 * LPS>(); return; } }
-    if constexpr (D >= 4) { if (later >= 2) { wait_vm<2 * LPS>(); return; } }
-    if constexpr (D >= 3) { if (later >= 1) { wait_vm<1 * LPS>(); return; } }
-    wait_vm<0>();
-}
-
-template <int F, int MT, int NW, int WN, int SPS, int D, int KMAX, int OUT>
+template <int F, int MT, int NW, int KMAX, int G, int OUT>
 __global__ __launch_bounds__(64 * NW)
 void mx_gemm_decode(GemmArgs p)
 {
-    using G = DecodeGeom<F, MT, NW, WN, SPS, D, KMAX>;
-    __shared__ __attribute__((aligned(1024))) char smem[G::BYTES];
+    using D = DecodeGeom<F, MT, NW, KMAX>;
+    constexpr int LB = 4;   // B loads per stage: 4 rows x 256 bytes each
+    static_assert(G >= 2 && G * LB + D::PA + 2 * D::PS < 64, "outstanding loads must fit the vmcnt field");
+    __shared__ __attribute__((aligned(1024))) char smem[D::BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int m0 = blockIdx.y * G::BM;
-    const int n0 = blockIdx.x * G::BN;
-    const int mrows = min(G::BM, p.M - m0);
-    const int nrows = min(G::BN, p.N - n0);
+    const int m0 = blockIdx.y * D::BM, n0 = blockIdx.x * D::BN;
+    const int mrows = min(D::BM, p.M - m0);
+    const int nrows = min(D::BN, p.N - n0);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * p.row_bytes, mrows * p.row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * p.row_bytes, nrows * p.row_bytes);
     const __amdgpu_buffer_rsrc_t rsa =
         make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
+    const int T = (int)((p.row_bytes + D::SW - 1) / D::SW);   // B stages
+    const int nst = p.nsteps;                                 // 128-K steps (<= NSTEP_MAX)
 
-    // 1. Resident A tile and scale codes, spread over the waves.  A row is
-    //    RS bytes in LDS (K*e of them valid); chunk c of row `row` sits at
-    //    chunk c ^ (row % 16).  Scale rows are SRS bytes, unswizzled.
+    // ---- B ring: load j of a stage covers rows 4j .. 4j+3 of this wave's 16
+    // (lane l: row 4j + l/16, bytes 16*(l%16) of the stage's 256)
+    const unsigned bload = (unsigned)(16 * wave + (lane >> 4)) * p.row_bytes + 16u * (unsigned)(lane & 15);
+    const unsigned bstride = 4u * p.row_bytes;
+    u4v stg[G][LB];
+    auto fill_stage = [&](u4v (&set)[LB], int t) {
+        if (t < T) {
 #pragma unroll
-    for (int i = 0; i < G::RPW; ++i) {
-        const int q = wave + NW * i;
-        if (q >= G::RJOBS) {
-            dma4(rsa, (lds_ptr_t)(smem + G::PAD_OFF), kOutOfRange);    // count padding
-            continue;
-        }
-        if (q < G::AJOBS) {
-            const int row = q / (G::RS / 1024);
-            const int cl = (q % (G::RS / 1024)) * 64 + lane;       // LDS chunk of this lane
-            const int cg = cl ^ (row & 15);                         // global chunk it holds
-            const unsigned off = (row < mrows && 16u * cg < p.row_bytes)
-                                     ? (unsigned)row * p.row_bytes + 16u * cg
-                                     : kOutOfRange;
-            dma16(ra, (lds_ptr_t)(smem + G::A_OFF + q * 1024), off);
+            for (int j = 0; j < LB; ++j)
+                set[j] = load16<CPOL_NONE>(rb, bload + (unsigned)j * bstride + (unsigned)t * D::SW);
         } else {
-            const int e = (q - G::AJOBS) * 1024 + 16 * lane;        // byte in [A rows | B rows] x SRS
-            const bool isa = (q - G::AJOBS) * 1024 < G::BM * G::SRS;   // wave-uniform
-            const int row = e / G::SRS, col = e % G::SRS;
-            const int rr = isa ? row : row - G::BM;
-            const unsigned off = (rr < (isa ? mrows : nrows) && (unsigned)col < p.srow_bytes)
-                                     ? (unsigned)rr * p.srow_bytes + (unsigned)col
-                                     : kOutOfRange;
-            dma16(isa ? rsa : rsb, (lds_ptr_t)(smem + G::SA_OFF + (q - G::AJOBS) * 1024), off);
-        }
-    }
-
-    // 2. This wave's B rows stream through its private ring.
-    char *ring = smem + G::RING_OFF + wave * D * G::SLOT;
-    const int nst = cdiv_c(p.nsteps, SPS);   // stages
-    auto issue = [&](int t) {
-        char *slot = ring + (t % D) * G::SLOT;
 #pragma unroll
-        for (int j = 0; j < G::LPS; ++j) {
-            const int row = j * G::RPB + lane / G::CPR;              // row within the wave's rows
-            const int c = (lane % G::CPR) ^ ((row / G::ROWS_PER_256) & G::SWZ_MASK);
-            const int step = t * SPS + c / (G::SB / 16);
-            const int brow = wave * G::BNW + row;                    // row within the tile
-            const unsigned off = (step < p.nsteps && brow < nrows)
-                                     ? (unsigned)brow * p.row_bytes + (unsigned)(t * SPS) * G::SB + 16u * c
-                                     : kOutOfRange;
-            dma16(rb, (lds_ptr_t)(slot + j * 1024), off);
+            for (int j = 0; j < LB; ++j)
+                set[j] = u4v{0u, 0u, 0u, 0u};
         }
     };
+    char *slots = smem + D::B_OFF + wave * 2 * D::SLOT;
+    const int bw_lane = D::b_off(lane >> 4, lane & 15);   // row l/16 of a 4-row load, chunk l%16
+    auto store_stage = [&](const u4v (&set)[LB], int t) {
+        char *slot = slots + (t & 1) * D::SLOT;
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i)
-        if (i < nst)
-            issue(i);
+        for (int j = 0; j < LB; ++j)
+            *reinterpret_cast<u4v *>(slot + bw_lane + D::b_off(4 * j, 0)) = set[j];
+    };
 
-    // resident loads were issued before any ring load: once at most the ring
-    // prologue is outstanding they have landed; the barrier makes every
-    // wave's share visible
-    decode_wait<G::LPS, D>(min(D - 1, nst));
-    block_barrier();
+    // ---- prologue: the first G B stages, then the A tile (flat: chunk i of
+    // the tile is bytes [16i, 16i+16) of rows m0.., i.e. row i / CH, chunk
+    // i % CH) and the scale dwords (flat: dword f of [A rows | B rows] is
+    // row f / NS, step f % NS), all in flight together
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        fill_stage(stg[i], i);
+    const unsigned CH = p.row_bytes / 16u;             // A chunks per row
+    const unsigned NS = (unsigned)nst;                  // scale dwords per row
+    const unsigned a_chunks = (unsigned)mrows * CH;
+    const unsigned s_dwords = (unsigned)(mrows + nrows) * NS;
+    u4v av[D::PA];
+    unsigned sv[D::PS];
+#pragma unroll
+    for (int i = 0; i < D::PA; ++i) {
+        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        av[i] = load16<CPOL_NONE>(ra, idx < a_chunks ? 16u * idx : kOutOfRange);
+    }
+#pragma unroll
+    for (int i = 0; i < D::PS; ++i) {
+        const unsigned f = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned fa = (unsigned)mrows * NS;       // A dwords come first
+        const bool isa = f < fa;
+        const unsigned off = f < s_dwords ? 4u * (isa ? f : f - fa) : kOutOfRange;
+        // one load may span A's and B's scale rows; a buffer resource must
+        // be uniform, so load from both with the other side's lanes out of
+        // range (they read 0)
+        sv[i] = load4(rsa, isa ? off : kOutOfRange) | load4(rsb, isa ? kOutOfRange : off);
+    }
+    wait_vm<0>();
+#pragma unroll
+    for (int i = 0; i < D::PA; ++i) {
+        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        if (idx < a_chunks) {
+            const unsigned row = idx / CH, c = idx % CH;
+            *reinterpret_cast<u4v *>(smem + D::a_off((int)row, (int)c)) = av[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D::PS; ++i) {
+        const unsigned f = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned fa = (unsigned)mrows * NS;
+        if (f < s_dwords) {
+            const bool isa = f < fa;
+            const unsigned ff = isa ? f : f - fa;
+            const unsigned row = ff / NS, k = ff % NS;
+            *reinterpret_cast<unsigned *>(smem + (isa ? D::SA_OFF + 4 * (k * D::BM + row)
+                                                      : D::SBS_OFF + 4 * (k * D::BN + row))) = sv[i];
+        }
+    }
+    __syncthreads();   // the A tile and scale codes are shared by all waves
 
-    v4f acc[MT][WN];
+    v4f acc[MT];
 #pragma unroll
     for (int x = 0; x < MT; ++x)
-#pragma unroll
-        for (int y = 0; y < WN; ++y)
-            acc[x][y] = v4f{0.f, 0.f, 0.f, 0.f};
+        acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const char *ares = smem + G::A_OFF;
-    const unsigned char *sres_a = reinterpret_cast<const unsigned char *>(smem + G::SA_OFF);
-    const unsigned char *sres_b =
-        reinterpret_cast<const unsigned char *>(smem + G::SB_OFF) + wave * G::BNW * G::SRS;
-    // One stage of MFMAs.  In the last, partial stage the steps past K are
-    // skipped: their B codes are zeros, but a resident scale row is loaded in
-    // 16-byte pieces, so its bytes past K/32 may hold the next row's codes
-    // (a NaN code there would poison the sum).
-    auto compute = [&](const char *slot, int t, auto tail) {
+    // one stage: store it, refill its staging set, then its MFMA steps
+    auto stage = [&](auto uc, int t) {
+        constexpr int u = decltype(uc)::value;
+        if (t + G - 1 < T)
+            wait_vm<(G - 1) * LB>();   // stage t's loads (the G-1 later stages may be in flight)
+        else
+            wait_vm<0>();
+        store_stage(stg[u], t);
+        fill_stage(stg[u], t + G);
+        const char *slot = slots + (t & 1) * D::SLOT;
 #pragma unroll
-        for (int s = 0; s < SPS; ++s) {
-            const int k = t * SPS + s;
-            if constexpr (decltype(tail)::value)
-                if (k >= p.nsteps) break;
-            StepFrag<F> fa[MT], fb[WN];
-            unsigned sa[MT], sb[WN];
+        for (int s = 0; s < D::SPS; ++s) {
+            const int k = t * D::SPS + s;   // global step
+            if (k >= nst)
+                break;
+            StepFrag<F> fb, fa[MT];
+            if constexpr (F == FMT_FP4) {
+                fb.d[0] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 4 * s + g));
+            } else {
+                fb.d[0] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + g));
+                fb.d[1] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + 4 + g));
+            }
+            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::BN + 16 * wave + r)) >> (8 * g);
+            unsigned sa[MT];
 #pragma unroll
             for (int x = 0; x < MT; ++x) {
                 const int row = 16 * x + r;
                 if constexpr (F == FMT_FP4) {
-                    fa[x].d[0] = *reinterpret_cast<const u4v *>(ares + G::a_off(row, 4 * k + g));
+                    fa[x].d[0] = *reinterpret_cast<const u4v *>(smem + D::a_off(row, 4 * k + g));
                 } else {
-                    fa[x].d[0] = *reinterpret_cast<const u4v *>(ares + G::a_off(row, 8 * k + g));
-                    fa[x].d[1] = *reinterpret_cast<const u4v *>(ares + G::a_off(row, 8 * k + 4 + g));
+                    fa[x].d[0] = *reinterpret_cast<const u4v *>(smem + D::a_off(row, 8 * k + g));
+                    fa[x].d[1] = *reinterpret_cast<const u4v *>(smem + D::a_off(row, 8 * k + 4 + g));
                 }
-                sa[x] = sres_a[row * G::SRS + 4 * k + g];
-            }
-#pragma unroll
-            for (int y = 0; y < WN; ++y) {
-                const int row = 16 * y + r;
-                if constexpr (F == FMT_FP4) {
-                    fb[y].d[0] = *reinterpret_cast<const u4v *>(slot + G::ring_off(row, 4 * s + g));
-                } else {
-                    fb[y].d[0] = *reinterpret_cast<const u4v *>(slot + G::ring_off(row, 8 * s + g));
-                    fb[y].d[1] = *reinterpret_cast<const u4v *>(slot + G::ring_off(row, 8 * s + 4 + g));
-                }
-                sb[y] = sres_b[row * G::SRS + 4 * k + g];
+                sa[x] = *reinterpret_cast<const unsigned *>(smem + D::SA_OFF + 4 * (k * D::BM + row)) >> (8 * g);
             }
 #pragma unroll
             for (int x = 0; x < MT; ++x)
-#pragma unroll
-                for (int y = 0; y < WN; ++y)
-                    acc[x][y] = mfma<F>(fb[y], sb[y], fa[x], sa[x], acc[x][y]);
+                acc[x] = mfma<F>(fb, sb, fa[x], sa[x], acc[x]);
         }
     };
-    const int nfull = p.nsteps / SPS;
-    for (int t = 0; t < nst; ++t) {
-        decode_wait<G::LPS, D>(min(D - 2, nst - 1 - t));
-        // the slot refilled below was last read by this wave's previous
-        // stage; its reads have completed
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (t + D - 1 < nst)
-            issue(t + D - 1);
-        const char *slot = ring + (t % D) * G::SLOT;
-        if (t < nfull)
-            compute(slot, t, std::false_type{});
-        else
-            compute(slot, t, std::true_type{});
-    }
+    for (int t0 = 0; t0 < T; t0 += G)
+        static_for<G>([&](auto uc) {
+            if (t0 + decltype(uc)::value < T)
+                stage(uc, t0 + decltype(uc)::value);
+        });
+    wait_vm<0>();
 
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int x = 0; x < MT; ++x) {
         const int m = m0 + 16 * x + r;
-#pragma unroll
-        for (int y = 0; y < WN; ++y) {
-            const int n = n0 + wave * G::BNW + 16 * y + 4 * g;
-            if (m < p.M && n < p.N)
-                store4<OUT>(p.c, p.N, m, n, acc[x][y], vec_ok && n + 3 < p.N);
-        }
+        const int n = n0 + 16 * wave + 4 * g;
+        if (m < p.M && n < p.N)
+            store4<OUT>(p.c, p.N, m, n, acc[x], vec_ok && n + 3 < p.N);
     }
 }
 

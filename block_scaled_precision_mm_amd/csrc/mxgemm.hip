@@ -17,6 +17,7 @@
 #include "../../include/mxgemm.h"
 #include "mx_decode.hpp"
 #include "mx_lds.hpp"
+#include "mx_skinny.hpp"
 #include "mx_stream.hpp"
 #include "mx_tile.hpp"
 
@@ -66,13 +67,22 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 // Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
 // (K up to K8 / K4 for FP8 / FP4), NW waves of NT B subtiles each streaming
 // through private rings of D stages of S8 / S4 steps.
-#define MXG_DFN(F, MT, NW, NT, S, D, KM, O) (&mx_gemm_decode<F, MT, NW, NT, S, D, KM, O>)
-#define MXG_DOUTS(F, MT, NW, NT, S, D, KM)                                                  \
-    {MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_BF16), MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_F16),  \
-     MXG_DFN(F, MT, NW, NT, S, D, KM, OUT_F32)}
-#define MXG_DECODE(NAME, MT, NW, NT, S4, S8, D, K4, K8)                                    \
-    {NAME, 16 * MT, 16 * NT * NW, 64 * NW,                                                 \
-     {MXG_DOUTS(FMT_FP8, MT, NW, NT, S8, D, K8), MXG_DOUTS(FMT_FP4, MT, NW, NT, S4, D, K4)}, {K8, K4}}
+#define MXG_DFN(F, MT, NW, KM, G, O) (&mx_gemm_decode<F, MT, NW, KM, G, O>)
+#define MXG_DOUTS(F, MT, NW, KM, G)                                                        \
+    {MXG_DFN(F, MT, NW, KM, G, OUT_BF16), MXG_DFN(F, MT, NW, KM, G, OUT_F16),                \
+     MXG_DFN(F, MT, NW, KM, G, OUT_F32)}
+#define MXG_DECODE(NAME, MT, NW, G, K4, K8)                                                \
+    {NAME, 16 * (MT), 16 * (NW), 64 * (NW),                                                \
+     {MXG_DOUTS(FMT_FP8, MT, NW, K8, G), MXG_DOUTS(FMT_FP4, MT, NW, K4, G)}, {K8, K4}, 0}
+
+// Decode-width tiles on the 32x32x64 instruction: waves split K, each
+// streams its run through a private register ring and LDS slot.
+#define MXG_KFN(F, MT, NT, KW, G, O) (&mx_gemm_skinny<F, MT, NT, KW, G, O>)
+#define MXG_KOUTS(F, MT, NT, KW, G) \
+    {MXG_KFN(F, MT, NT, KW, G, OUT_BF16), MXG_KFN(F, MT, NT, KW, G, OUT_F16), MXG_KFN(F, MT, NT, KW, G, OUT_F32)}
+#define MXG_SKINNY(NAME, MT, NT, KW, G)                                             \
+    {NAME, 32 * (MT), 32 * (NT), 64 * (KW),                                         \
+     {MXG_KOUTS(FMT_FP8, MT, NT, KW, G), MXG_KOUTS(FMT_FP4, MT, NT, KW, G)}, {0, 0}, 0}
 
 // Large tiles on the 32x32x64 instruction, staged through registers.
 #define MXG_TFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O>)
@@ -100,13 +110,12 @@ const Variant kVariants[] = {
     MXG_LDS("lds_32x64_w4",        1, 1, 4, 2, 1, 4, 2, 4, 4),
     MXG_LDS("lds_64x16_k4",        4, 1, 1, 4, 1, 2, 1, 3, 3),
     MXG_LDS("lds_32x32_k4",        4, 1, 1, 2, 2, 2, 1, 3, 3),
-    MXG_LDS("lds_64x64_w2x2",      1, 2, 2, 2, 2, 4, 2, 3, 3),
-    MXG_LDS("lds_128x128_w2x2",    1, 2, 2, 4, 4, 2, 1, 3, 3),
-    MXG_LDS("lds_256x128_w2x2",    1, 2, 2, 8, 4, 1, 1, 3, 3),
-    MXG_LDS("lds_256x256_w2x2",    1, 2, 2, 8, 8, 1, 1, 3, 2),
     //          name              MT NW NT S4 S8 D  K4    K8
-    MXG_DECODE("decode_32x64",    2, 4, 1, 4, 2, 5, 4096, 2048),
-    MXG_DECODE("decode_16x64",    1, 4, 1, 4, 2, 6, 4096, 2048),
+    MXG_DECODE("decode_32x64",    2, 4, 4, 4096, 2048),
+    MXG_DECODE("decode_16x64",    1, 4, 4, 4096, 2048),
+
+    MXG_SKINNY("skinny_32x64_k4",   1, 2, 4, 4),
+    MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
 
     MXG_TILE("tile_256x256",      4, 4),
     MXG_TILE("tile_256x128",      4, 2),
@@ -184,7 +193,9 @@ int find_variant(const char *name)
 }
 
 // Default tile choice, from measured sweeps on MI355X.  Up to 64 rows of A
-// the product is a B stream and the register-streaming kernel wins; beyond
+// the product is a B stream and the register-streaming kernel wins (at 33-64
+// rows and wide N the split-K skinny tile, which reads A once per
+// workgroup); beyond
 // that the register-staged tile kernels take over, with the largest tile
 // that still gives every compute unit work (per-CU traffic is proportional
 // to tile rows + tile columns, so bigger tiles move fewer bytes per FLOP).
@@ -197,7 +208,7 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     if (M <= 32)
         return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
     if (M <= 64)
-        return find_variant("stream_2x2_k4");
+        return find_variant(N >= 8192 ? "skinny_64x64_k4" : "stream_2x2_k4");
     if (cdiv(M, 256) * cdiv(N, 256) >= 384)
         return find_variant("tile_256x256");
     if (cdiv(M, 256) * cdiv(N, 128) >= 192)
