@@ -62,8 +62,10 @@ def _load():
     lib.mx_oracle_gemm_at.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, P, P, I64, P, P]
     lib.mx_oracle_round_bf16.argtypes = [P, I64, P]
     lib.mx_oracle_round_f16.argtypes = [P, I64, P]
+    lib.mx_oracle_quantize.argtypes = [ctypes.c_int, P, I64, I64, P, P]
     for f in (lib.mx_oracle_decode, lib.mx_oracle_decode_scale, lib.mx_oracle_gemm,
-              lib.mx_oracle_gemm_at, lib.mx_oracle_round_bf16, lib.mx_oracle_round_f16):
+              lib.mx_oracle_gemm_at, lib.mx_oracle_round_bf16, lib.mx_oracle_round_f16,
+              lib.mx_oracle_quantize):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -155,3 +157,23 @@ def round_f16(x) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint16)
     lib.mx_oracle_round_f16(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def quantize(fmt: str, x_bf16, rows: int, K: int):
+    """MX-quantize BF16 rows (uint16 bit patterns, [rows][K], K % 32 == 0) along K.
+
+    Returns (codes, scales): codes [rows][K/2] (fp4, two per byte, even k low
+    nibble) or [rows][K] (fp8) uint8, scales [rows][K/32] E8M0 uint8.  The
+    rule (OCP MX v1.0 conversion; the pages only name BlockWise1x32 E8M0
+    scales, "PyTorch 接上 FlyDSL", 5ulink.com, 支持边界): scale code =
+    floor(log2 amax) - emax + 127 clamped to [0, 254] (emax 2 / 8, 0 for an
+    all-zero block, 0xFF for a block holding NaN or Inf); elements rounded to
+    the nearest code, ties to even, saturating; sign from the input.
+    """
+    x = np.ascontiguousarray(np.asarray(x_bf16, dtype=np.uint16).reshape(rows, K))
+    codes = np.zeros((rows, K // 2 if fmt == "fp4" else K), dtype=np.uint8)
+    scales = np.zeros((rows, K // 32), dtype=np.uint8)
+    rc = _load().mx_oracle_quantize(FMT[fmt], _ptr(x), rows, K, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("mx_oracle_quantize: invalid arguments")
+    return codes, scales

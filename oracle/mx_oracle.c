@@ -264,4 +264,108 @@ int mx_oracle_round_f16(const double *x, int64_t n, uint16_t *out)
     return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * MX quantization: BF16 rows -> element codes + one E8M0 scale per 32
+ * consecutive K values (the step before the GEMM; "PyTorch 接上 FlyDSL",
+ * 5ulink.com, paragraph under the support matrix: BlockWise1x32 E8M0
+ * scales).  The conversion rule is not spelled out on the pages; this
+ * follows the OCP MX v1.0 conversion (shared exponent from the block's
+ * largest magnitude, elements rounded to nearest even and saturated):
+ *
+ *   1. decode the 32 BF16 values of the block to double;
+ *   2. a block holding a NaN or an infinity gets scale code 0xFF (NaN) and
+ *      element codes 0;
+ *   3. amax = max |x|; scale code s = floor(log2 amax) - emax + 127 clamped
+ *      to [0, 254], emax = 2 (E2M1) or 8 (E4M3); an all-zero block gets 0;
+ *   4. each element: v = |x| / 2^(s-127), replaced by the representable
+ *      magnitude nearest to v (searched over every non-NaN code), ties to
+ *      the code with an even last bit (= even mantissa); magnitudes beyond
+ *      the largest code take the largest code (saturation); the sign bit is
+ *      the sign bit of x;
+ *   5. FP4 codes are packed two per byte, even k in the low nibble.
+ * ------------------------------------------------------------------------ */
+static double bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* nearest non-negative code to v >= 0; ties to the even code */
+static int nearest_code(int fmt, double v)
+{
+    int best = 0, ncodes = (fmt == MXO_FMT_FP4) ? 8 : 128;
+    double bestd = INFINITY;
+    for (int c = 0; c < ncodes; ++c) {
+        double q = (fmt == MXO_FMT_FP4) ? tab_e2m1[c] : tab_e4m3[c];
+        if (isnan(q))
+            continue;
+        double d = fabs(v - q);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+int mx_oracle_quantize(int fmt, const uint16_t *x, int64_t rows, int64_t K,
+                       uint8_t *codes, uint8_t *scales)
+{
+    if ((fmt != MXO_FMT_FP4 && fmt != MXO_FMT_FP8) || rows < 0 || K <= 0 || K % 32)
+        return -1;
+    build_tables();
+    const int emax = (fmt == MXO_FMT_FP4) ? 2 : 8;
+    const int sbit = (fmt == MXO_FMT_FP4) ? 8 : 128;
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + r * K + 32 * b;
+            double val[32];
+            int special = 0;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                val[j] = bf16_value(xb[j]);
+                if (isnan(val[j]) || isinf(val[j]))
+                    special = 1;
+                else if (fabs(val[j]) > amax)
+                    amax = fabs(val[j]);
+            }
+            int s, q[32];
+            if (special) {
+                s = 255;
+                for (int j = 0; j < 32; ++j)
+                    q[j] = 0;
+            } else {
+                if (amax == 0.0) {
+                    s = 0;
+                } else {
+                    int ex;
+                    frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1) */
+                    s = (ex - 1) - emax + 127;
+                    if (s < 0) s = 0;
+                    if (s > 254) s = 254;
+                }
+                for (int j = 0; j < 32; ++j) {
+                    double v = ldexp(fabs(val[j]), 127 - s);
+                    q[j] = nearest_code(fmt, v) | (signbit(val[j]) ? sbit : 0);
+                }
+            }
+            scales[r * nb + b] = (uint8_t)s;
+            if (fmt == MXO_FMT_FP4) {
+                uint8_t *cb = codes + r * (K / 2) + 16 * b;
+                for (int j = 0; j < 16; ++j)
+                    cb[j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+            } else {
+                uint8_t *cb = codes + r * K + 32 * b;
+                for (int j = 0; j < 32; ++j)
+                    cb[j] = (uint8_t)q[j];
+            }
+        }
+    }
+    return 0;
+}
+
 int mx_oracle_abi_version(void) { return 1; }
