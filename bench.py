@@ -91,16 +91,22 @@ def copy_calibration(nbytes, steps):
                       "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def host_threads():
+    """Threads the OpenMP oracle runs on: the affinity set, capped by OMP_NUM_THREADS."""
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp:
+        cores = min(cores, int(omp))
+    return cores
+
+
 def cpu_baseline(cs, budget_s):
     """The oracle, as it stands, on the host cores: whole output rows of the
     workload, as many as fit the time budget (at least one)."""
     import numpy as np
     import oracle
     oracle.build()
-    cores = len(os.sched_getaffinity(0))
-    omp = os.environ.get("OMP_NUM_THREADS")
-    if omp:
-        cores = min(cores, int(omp))
+    cores = host_threads()
     # calibrate on one row, then run a bounded block of rows; if the whole
     # workload is cheaper than the budget, repeat it to fill the budget
     t0 = time.perf_counter()
@@ -122,6 +128,115 @@ def cpu_baseline(cs, budget_s):
             "seconds_per_full_workload": dt / reps * cs.M / rows}
 
 
+def parse_quant_workload(name):
+    """quant_<fp4|fp8>_<rows>x<K>: MX quantization of a BF16 [rows, K] matrix."""
+    parts = name.split("_")
+    if len(parts) != 3 or parts[0] != "quant" or parts[1] not in ("fp4", "fp8"):
+        raise SystemExit("unknown quantize workload %r (expected quant_<fp4|fp8>_<rows>x<K>)" % name)
+    rows, K = (int(v) for v in parts[2].split("x"))
+    if K % 32:
+        raise SystemExit("K must be a multiple of 32")
+    return parts[1], rows, K
+
+
+def cpu_baseline_quant(fmt, xbits, budget_s):
+    """The oracle's quantizer, as it stands, on whole rows of the input."""
+    import oracle
+    oracle.build()
+    cores = host_threads()
+    rows, K = xbits.shape
+    t0 = time.perf_counter()
+    oracle.quantize(fmt, xbits[:1], 1, K)
+    t_row = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(rows, budget_s / t_row)))
+    t0 = time.perf_counter()
+    oracle.quantize(fmt, xbits[:n], n, K)
+    dt = time.perf_counter() - t0
+    elems = float(n) * K
+    return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d rows (K=%d), %.2f s" % (n, rows, K, dt)}
+
+
+def bench_quant(args):
+    """One step = one MX quantization of a BF16 matrix (input resident in
+    HBM, rotated sets as for the GEMM); bound: HBM, algorithmic bytes =
+    rows*K*(2 + e) + rows*K/32 (e = 1/2 E2M1, 1 E4M3)."""
+    import numpy as np
+    import torch
+
+    import mxgen
+    import block_scaled_precision_mm_amd as mx
+
+    fmt, rows, K = parse_quant_workload(args.workload)
+    is_fp4 = fmt == "fp4"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    xf = mxgen.normal_bf16(7001, (rows, K))
+    xbits = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    cbytes = rows * K // 2 if is_fp4 else rows * K
+    set_bytes = rows * K * 2 + cbytes + rows * K // 32
+    R = 1 if args.rotate_bytes <= 0 else max(1, math.ceil(args.rotate_bytes / set_bytes))
+    R = min(R, 4096)
+    x0 = torch.from_numpy(xbits.view(np.int16)).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    cs = [torch.empty(cbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    ss = [torch.empty(rows * K // 32, dtype=torch.uint8, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    st_ptr = stream.cuda_stream
+    ptrs = [(x.data_ptr(), c.data_ptr(), s_.data_ptr()) for x, c, s_ in zip(xs, cs, ss)]
+
+    def step(i):
+        x, c, s_ = ptrs[i % R]
+        rc = mx._lib.mx_quantize_bf16(x, c, s_, rows, K, 1 if is_fp4 else 0, st_ptr)
+        if rc:
+            raise mx.MxGemmError(rc, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    Ksteps = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for _ in range(max(8, Ksteps // 4)):
+        filler.add_(1.0)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(Ksteps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / Ksteps
+    del filler
+    alg = float(set_bytes)
+    achieved = alg / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "mx_quantize_" + fmt, "algorithmic_bytes": int(alg),
+            "kernel_us": round(ms * 1e3, 3), "roofline_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 3)}
+    rec = recorded_traffic(args.workload, roof["kernel"])
+    if rec is not None:
+        roof["traffic"] = rec["hbm_bytes_per_launch"]
+        roof["traffic_unit"] = "bytes/launch"
+        roof["traffic_vs_algorithmic"] = round(rec["hbm_bytes_per_launch"] / alg, 3)
+    out = {
+        "metric": "MX quantization throughput (BF16 -> %s + E8M0/32) on 1 MI355X" % ("E2M1" if is_fp4 else "E4M3"),
+        "value": round(rows * K / (ms * 1e-3) / 1e9, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1, "steps": Ksteps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->" + ("e2m1" if is_fp4 else "e4m3"), "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "K": K, "recipe": "bf16-rounded N(0,1), seed 7001",
+                   "rotating_sets": R},
+        "roofline": roof,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_quant(fmt, xbits, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,6 +245,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.workload.startswith("quant_"):
+        bench_quant(args)
         return
     import numpy as np
     import torch

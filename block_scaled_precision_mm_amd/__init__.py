@@ -51,14 +51,15 @@ _lib.mx_status_string.argtypes = [_INT]
 _lib.mx_status_string.restype = ctypes.c_char_p
 _lib.mx_variant_name.argtypes = [_INT]
 _lib.mx_variant_name.restype = ctypes.c_char_p
+_lib.mx_quantize_bf16.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
-           "mx_last_hip_error", "mx_abi_version", "mx_default_variant"):
+           "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
 EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
-           "mx_last_hip_error", "mx_abi_version")
+           "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16")
 
 
 class MxGemmError(RuntimeError):
@@ -172,6 +173,26 @@ def mx_last_hip_error() -> int:
 
 def mx_abi_version() -> int:
     return int(_lib.mx_abi_version())
+
+
+def mx_quantize_bf16(x, codes, scales, rows: int, K: int, is_fp4: bool, stream=None) -> None:
+    """MX-quantize BF16 rows along K on the GPU (C ABI mx_quantize_bf16).
+
+    x: bfloat16 [rows][K] (or a raw device pointer); codes: uint8 [rows][K/2]
+    (E2M1, two per byte, even k low nibble) or [rows][K] (E4M3); scales:
+    uint8 [rows][K/32] E8M0.  Argument marshalling only.
+    """
+    if isinstance(x, torch.Tensor):
+        if not x.is_cuda or not x.is_contiguous() or x.element_size() != 2 or x.numel() != rows * K:
+            raise ValueError("x must be a contiguous 2-byte CUDA tensor with rows*K elements")
+    for name, t, n in (("codes", codes, rows * (K // 2 if is_fp4 else K)), ("scales", scales, rows * (K // 32))):
+        if isinstance(t, torch.Tensor):
+            if not t.is_cuda or not t.is_contiguous() or t.element_size() != 1 or t.numel() != n:
+                raise ValueError("%s must be a contiguous 1-byte CUDA tensor of %d elements" % (name, n))
+    rc = _lib.mx_quantize_bf16(_ptr(x), _ptr(codes), _ptr(scales), rows, K, 1 if is_fp4 else 0,
+                               _stream(stream))
+    if rc != 0:
+        raise MxGemmError(rc, "mx_quantize_bf16")
 
 
 # ------------------------------------------------------------- convenience

@@ -12,11 +12,13 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/mxgemm.h"
 #include "mx_decode.hpp"
 #include "mx_lds.hpp"
+#include "mx_quant.hpp"
 #include "mx_skinny.hpp"
 #include "mx_stream.hpp"
 #include "mx_tile.hpp"
@@ -343,6 +345,37 @@ const char *mx_status_string(int status)
     case MXG_ERR_CONFIG: return "invalid kernel variant";
     default: return "unknown status";
     }
+}
+
+int mx_quantize_bf16(const void *x, void *codes, void *scales, int64_t rows, int64_t K,
+                     int is_fp4, mxg_stream_t stream)
+{
+    if (!x || !codes || !scales)
+        return MXG_ERR_NULL;
+    if (rows < 1 || K < 1 || rows > ((int64_t)1 << 40) / K)
+        return MXG_ERR_SHAPE;
+    if (K % 32)
+        return MXG_ERR_K_ALIGN;
+    if (((uintptr_t)x & 15) || ((uintptr_t)codes & 15))
+        return MXG_ERR_PTR_ALIGN;
+    int rc = check_device();
+    if (rc)
+        return rc;
+    const long long nblocks = (long long)(rows * (K / 32));
+    const long long tiles = (nblocks + 63) / 64;                     // one per wave
+    const unsigned grid = (unsigned)std::min<long long>((tiles + 3) / 4, 16384);
+    if (is_fp4)
+        hipLaunchKernelGGL(mx_quantize<FMT_FP4>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                           (const uint16_t *)x, (uint8_t *)codes, (uint8_t *)scales, nblocks);
+    else
+        hipLaunchKernelGGL(mx_quantize<FMT_FP8>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                           (const uint16_t *)x, (uint8_t *)codes, (uint8_t *)scales, nblocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXG_ERR_HIP;
+    }
+    return MXG_OK;
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

@@ -113,6 +113,34 @@ int64_t mx_variant_max_k(int variant, int is_fp4);
 /* Human-readable name of a variant (tile shape), or NULL if out of range. */
 const char *mx_variant_name(int variant);
 
+/*
+ * MX quantization, the step before the GEMM ("PyTorch 接上 FlyDSL",
+ * 5ulink.com, paragraph under the support matrix: one E8M0 scale per 32
+ * values, BlockWise1x32).  Quantizes rows x 32-value blocks of BF16 values
+ * along K, in the operand layout mx_scaled_mm_fp4/fp8 take (apply it to A
+ * [M][K] and to B as [N][K]).  Per block (OCP MX v1.0 conversion; the pages
+ * do not spell it out): scale code = floor(log2 amax) - emax + 127 clamped
+ * to [0, 254] (emax 2 for E2M1, 8 for E4M3; 0 for an all-zero block; 0xFF
+ * for a block holding a NaN or an infinity, whose element codes are 0);
+ * each element |x| / 2^(code-127) rounded to the nearest E2M1/E4M3 code,
+ * ties to even, saturating at the largest finite code; sign copied from x.
+ *
+ * x            BF16 bit patterns [rows][K], 16-byte aligned.
+ * codes        output: E2M1 [rows][K/2] bytes (two codes per byte, even k in
+ *              the low nibble) or E4M3 [rows][K] bytes; 16-byte aligned.
+ * scales       output: E8M0 codes [rows][K/32].
+ * rows, K      rows >= 1; K a positive multiple of 32.
+ * is_fp4       1: E2M1 codes (MXFP4); 0: E4M3 codes (MXFP8).
+ * stream       HIP stream the work is enqueued on (0 = null stream).
+ *
+ * Returns MXG_OK after enqueueing, or an error with nothing enqueued:
+ * MXG_ERR_NULL, MXG_ERR_SHAPE (rows or K < 1, rows*K > 2^40),
+ * MXG_ERR_K_ALIGN (K % 32 != 0), MXG_ERR_PTR_ALIGN, MXG_ERR_DEVICE,
+ * MXG_ERR_HIP.  The caller owns all buffers; nothing is allocated.
+ */
+int mx_quantize_bf16(const void *x, void *codes, void *scales, int64_t rows, int64_t K,
+                     int is_fp4, mxg_stream_t stream);
+
 /* The variant the default entry points pick for a shape (>= 0), or a
  * negative status for an invalid shape. */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
@@ -125,7 +153,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 2
+#define MXGEMM_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,7 @@ def lib():
     L.mx_default_variant.argtypes = [INT, I64, I64, I64]
     L.mx_variant_max_k.argtypes = [INT, INT]
     L.mx_variant_max_k.restype = I64
+    L.mx_quantize_bf16.argtypes = [P, P, P, I64, I64, INT, P]
     return L
 
 
@@ -55,7 +56,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 2
+    assert lib.mx_abi_version() == 3
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -95,6 +96,22 @@ A = 0x10000   # fake but aligned device addresses: validation never dereferences
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(lib, fn, args, status):
     rc = getattr(lib, fn)(*args, None)
+    assert rc == status, (rc, lib.mx_status_string(rc))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, A, A, 4, 64, 1), -1),              # null x
+    ((A, 0, A, 4, 64, 0), -1),              # null codes
+    ((A, A, 0, 4, 64, 1), -1),              # null scales
+    ((A, A, A, 0, 64, 1), -2),              # rows = 0
+    ((A, A, A, 4, 0, 1), -2),               # K = 0
+    ((A, A, A, 1 << 30, 1 << 12, 1), -2),   # rows * K beyond 2^40
+    ((A, A, A, 4, 48, 1), -3),              # K % 32 != 0
+    ((A + 2, A, A, 4, 64, 1), -4),          # x not 16-byte aligned
+    ((A, A + 8, A, 4, 64, 0), -4),          # codes not 16-byte aligned
+])
+def test_quantize_invalid_arguments(lib, args, status):
+    rc = lib.mx_quantize_bf16(*args, None)
     assert rc == status, (rc, lib.mx_status_string(rc))
 
 

@@ -93,3 +93,20 @@ def test_scale_shift_perturbation_count():
     t = mxgen._shift_blocks(s, 0.01, 8, 7)
     d = t.astype(int) - s.astype(int)
     assert (d != 0).sum() == 40 and set(np.unique(d[d != 0])) <= {-8, 8}
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_generator_encoder_agrees_with_oracle_quantizer(fmt):
+    # the generator's numpy encoder (input synthesis) and the oracle's C
+    # quantizer are written independently; on finite bf16 data they must give
+    # the same MX codes, so every GEMM input is what the quantization rule makes
+    import oracle
+    x = mxgen.normal_bf16(41, (96, 512), sigma=3.0)
+    x[5, :64] *= np.float32(1e-30)
+    x[9, 32:64] = 0.0
+    x = mxgen.round_to_bf16(x)
+    codes, scales = mxgen.quantize(x, fmt)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    oc, os_ = oracle.quantize(fmt, bits, 96, 512)
+    assert np.array_equal(scales, os_)
+    assert np.array_equal(codes, oc)
