@@ -48,15 +48,35 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources of the library: counter-derived traffic
-    figures are only reported for the kernels they were measured on."""
+KERNEL_HEADER = {"stream_": "mx_stream.hpp", "lds_": "mx_lds.hpp", "tile_": "mx_tile.hpp",
+                 "skinny_": "mx_skinny.hpp", "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp"}
+
+
+def kernel_source_digest(kernel_name):
+    """sha256 over the sources a kernel is built from (its header, the
+    headers that one includes, the variant table and the build flags):
+    counter-derived traffic figures are only reported for the kernels they
+    were measured on."""
     import hashlib
-    h = hashlib.sha256()
+    import re
     csrc = os.path.join(ROOT, "block_scaled_precision_mm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    head = next((h for p, h in KERNEL_HEADER.items() if kernel_name.startswith(p)), None)
+    if head is None:
+        return None
+    todo, seen = [head], set()
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            todo += re.findall(r'#include "([^"/]+)"', f.read())
+    files = [os.path.join(csrc, n) for n in sorted(seen)]
+    files += [os.path.join(csrc, "mxgemm.hip"), os.path.join(ROOT, "block_scaled_precision_mm_amd", "build.py")]
+    h = hashlib.sha256()
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -68,7 +88,7 @@ def recorded_traffic(workload, variant_name):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("source_digest") != kernel_source_digest() or rec.get("kernel") != variant_name:
+    if not rec or rec.get("kernel") != variant_name or rec.get("source_digest") != kernel_source_digest(variant_name):
         return None
     return rec
 

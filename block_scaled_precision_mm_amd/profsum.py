@@ -116,7 +116,7 @@ def main(argv=None):
         import bench
         rec = {
             "kernel": args.kernel_name,
-            "source_digest": bench.kernel_source_digest(),
+            "source_digest": bench.kernel_source_digest(args.kernel_name),
             "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
             "copy_kernel": ck, "copy_bytes": args.copy_bytes,
             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
