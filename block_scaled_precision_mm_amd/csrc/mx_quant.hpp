@@ -15,7 +15,12 @@
 // wave reads 1 KB contiguous (lane l: bytes 1024j + 16l of the wave's 4 KB
 // tile), so the four lanes 4q..4q+3 hold one 32-value block and combine
 // their maxima with two DPP quad permutations; code stores are contiguous
-// per instruction too.
+// per instruction too.  The input is read once, so its loads are marked
+// nontemporal: on MI355X (8192 x 8192 BF16) that took E2M1 from 31.0 to
+// 26.6-27.1 us (6.3 TB/s) and E4M3 from 36.5 to 34.5 us, where a plain
+// kernel streaming the same bytes (16 B read, 4 B written per lane) takes
+// 29.2 us; more tiles in flight per wave (2 or 4) and other grid sizes were
+// slower or equal.
 //
 // The rounding is done by gfx950's scaled conversions
 // (v_cvt_scalef32_pk_fp4_bf16 / v_cvt_scalef32_pk_fp8_bf16: two BF16 values
@@ -90,7 +95,7 @@ void mx_quantize(const uint16_t *x, uint8_t *codes, uint8_t *scales, long long n
             const long long b = tile * 64 + 16 * j + (lane >> 2);    // this lane's block
             w[j] = u4v{0u, 0u, 0u, 0u};
             if (b < nblocks)
-                w[j] = *reinterpret_cast<const u4v *>(x + tile * 2048 + 512 * j + 8 * lane);
+                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(x + tile * 2048 + 512 * j + 8 * lane));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
