@@ -37,10 +37,10 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 -> float32 holding the nearest bf16 value (ties to even).
     Inputs are finite (normal draws); NaN/Inf are not produced here."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    # finite inputs: u <= 0xFF7FFFFF, so u + 0x8000 cannot wrap in uint32
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
+    return r.view(np.float32)
 
 
 def normal_bf16(seed: int, shape: Tuple[int, int], sigma: float = 1.0,
@@ -245,3 +245,75 @@ def case(name: str) -> Case:
 def case_shape(name: str) -> Tuple[str, int, int, int]:
     s = NAMED[name]
     return s["fmt"], s["M"], s["N"], s["K"]
+
+
+# ------------------------------------------------------------ grouped inputs
+
+@dataclasses.dataclass
+class GroupedCase:
+    name: str
+    fmt: str
+    G: int
+    M: int               # rows of A over all groups
+    N: int
+    K: int
+    sizes: np.ndarray    # rows per group (int64 [G]); zeros are empty groups
+    offs: np.ndarray     # cumulative ends (int32 [G]), as the grouped entry points take them
+    a: np.ndarray        # packed A [M][K/2 or K]
+    b: np.ndarray        # packed B [G*N][K/2 or K] (group-major)
+    sa: np.ndarray       # [M][K/32]
+    sb: np.ndarray       # [G*N][K/32]
+    recipe: str
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> float:
+        """A, the B operands (and scales) of the non-empty groups, C."""
+        e = 0.5 if self.fmt == "fp4" else 1.0
+        used = int(np.count_nonzero(self.sizes))
+        return (self.M + used * self.N) * self.K * (e + 1.0 / 32) + self.M * self.N * out_bytes
+
+
+def grouped_sizes(seed: int, G: int, M: int, n_empty: int, skew: float = 0.8) -> np.ndarray:
+    """Rows per group for an unbalanced mixture-of-experts routing: n_empty
+    groups get no rows; the others draw M rows multinomially with weights
+    1/(rank+1)^skew over a seeded random ranking."""
+    rng = np.random.default_rng(seed)
+    live = np.sort(rng.choice(G, size=G - n_empty, replace=False))
+    w = 1.0 / (rng.permutation(len(live)) + 1.0) ** skew
+    sizes = np.zeros(G, dtype=np.int64)
+    sizes[live] = rng.multinomial(M, w / w.sum())
+    return sizes
+
+
+def make_grouped_case(name: str, fmt: str, G: int, M: int, N: int, K: int, case_id: int,
+                      n_empty: int = 0, sigma_b: float = 1.0) -> GroupedCase:
+    """Seeded recipe: seed = 1000*case_id + {A: 1, B: 2, group sizes: 6}."""
+    sizes = grouped_sizes(1000 * case_id + 6, G, M, n_empty)
+    xa = normal_bf16(1000 * case_id + 1, (M, K))
+    a, sa = quantize(xa, fmt)
+    del xa
+    xb = normal_bf16(1000 * case_id + 2, (G * N, K), sigma_b)
+    b, sb = quantize(xb, fmt)
+    del xb
+    recipe = ("A~N(0,1) B~N(0,%g), %d groups, %d empty, rows per group %s"
+              % (sigma_b, G, n_empty, ",".join(str(int(s)) for s in sizes)))
+    offs = np.cumsum(sizes).astype(np.int32)
+    return GroupedCase(name, fmt, G, M, N, K, sizes, offs, a, b, sa, sb, recipe)
+
+
+# Grouped workloads.  The pages run 24 unlisted grouped-GEMM cases, five of
+# them with unbalanced experts including empty ones; these stand in for
+# them at the MXFP8 precision of the roadmap's grouped kernel: a prefill
+# batch over 8 experts (8192 routed rows, one expert empty) and a decode
+# step over 32 experts (256 routed rows, 5 experts empty).
+GROUPED = {
+    "g1_fp8_8x8192x4096x4096": dict(fmt="fp8", G=8, M=8192, N=4096, K=4096, case_id=201, n_empty=1),
+    "g2_fp8_32x256x2048x2048": dict(fmt="fp8", G=32, M=256, N=2048, K=2048, case_id=202, n_empty=5),
+}
+
+
+def grouped_case(name: str) -> GroupedCase:
+    return make_grouped_case(name, **GROUPED[name])

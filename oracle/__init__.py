@@ -141,6 +141,43 @@ def gemm_at(fmt: str, a, b, sa, sb, M: int, N: int, K: int, ms, ns):
     return c, s
 
 
+def group_rows(offs, groups: int, M: int):
+    """Row ranges [start, end) of each group of a grouped product: group g
+    ends at offs[g] (cumulative sizes, "PyTorch 接上 FlyDSL" support-matrix
+    row "Grouped GEMM": groups of A may differ in length, empty groups are
+    skipped), with the library's documented reading of arbitrary offs: the
+    ends are made non-decreasing and clamped into [0, M]."""
+    offs = np.asarray(offs, dtype=np.int64).reshape(groups)
+    ranges = []
+    end = 0
+    for g in range(groups):
+        start = end
+        end = min(M, max(int(offs[g]), start))
+        ranges.append((start, end))
+    return ranges
+
+
+def grouped_gemm(fmt: str, a, b, sa, sb, offs, groups: int, M: int, N: int, K: int):
+    """Grouped product, group by group: rows [start_g, end_g) of A (and of its
+    scales) times B[g] ([groups][N][K] operand, [groups][N][K/32] scales)
+    with the plain oracle GEMM.  Returns (c, s, covered): float64 [M, N]
+    values and sum |a_k b_k| (NaN in rows no group covers) and the bool
+    [M] mask of covered rows."""
+    rb = _row_bytes(fmt, K)
+    a = _u8(a).reshape(M, rb) if M else _u8(a).reshape(0, rb)
+    sa = _u8(sa).reshape(M, K // 32) if M else _u8(sa).reshape(0, K // 32)
+    b = _u8(b).reshape(groups, N, rb)
+    sb = _u8(sb).reshape(groups, N, K // 32)
+    c = np.full((M, N), np.nan)
+    s = np.full((M, N), np.nan)
+    covered = np.zeros(M, dtype=bool)
+    for g, (r0, r1) in enumerate(group_rows(offs, groups, M)):
+        if r1 > r0:
+            c[r0:r1], s[r0:r1] = gemm(fmt, a[r0:r1], b[g], sa[r0:r1], sb[g], r1 - r0, N, K)
+            covered[r0:r1] = True
+    return c, s, covered
+
+
 def round_bf16(x) -> np.ndarray:
     """float64 -> bf16 bit patterns (uint16), round-to-nearest-even, direct."""
     lib = _load()
