@@ -52,14 +52,24 @@ _lib.mx_status_string.restype = ctypes.c_char_p
 _lib.mx_variant_name.argtypes = [_INT]
 _lib.mx_variant_name.restype = ctypes.c_char_p
 _lib.mx_quantize_bf16.argtypes = [_P, _P, _P, _I64, _I64, _INT, _P]
+_lib.mx_grouped_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _P]
+_lib.mx_grouped_mm_fp8.argtypes = _lib.mx_grouped_mm_fp4.argtypes
+_lib.mx_grouped_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _INT, _P]
+_lib.mx_grouped_variant_name.argtypes = [_INT]
+_lib.mx_grouped_variant_name.restype = ctypes.c_char_p
+_lib.mx_grouped_default_variant.argtypes = [_I64, _I64, _I64]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
-           "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16"):
+           "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
+           "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
+           "mx_grouped_num_variants", "mx_grouped_default_variant"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
 EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
-           "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16")
+           "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16",
+           "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
+           "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant")
 
 
 class MxGemmError(RuntimeError):
@@ -193,6 +203,65 @@ def mx_quantize_bf16(x, codes, scales, rows: int, K: int, is_fp4: bool, stream=N
                                _stream(stream))
     if rc != 0:
         raise MxGemmError(rc, "mx_quantize_bf16")
+
+
+def _check_grouped(is_fp4, a, b, sa, sb, c, offs, groups, M, N, K):
+    eb = K // 2 if is_fp4 else K
+    for name, t, n in (("a", a, M * eb), ("b", b, groups * N * eb), ("a_scale", sa, M * (K // 32)),
+                       ("b_scale", sb, groups * N * (K // 32))):
+        if isinstance(t, torch.Tensor):
+            if not t.is_cuda or not t.is_contiguous() or t.element_size() != 1 or t.numel() != n:
+                raise ValueError("%s must be a contiguous 1-byte CUDA tensor of %d bytes" % (name, n))
+    if isinstance(c, torch.Tensor):
+        if not c.is_cuda or not c.is_contiguous() or c.numel() != M * N:
+            raise ValueError("c must be a contiguous CUDA tensor with M*N elements")
+    if isinstance(offs, torch.Tensor):
+        if not offs.is_cuda or offs.dtype != torch.int32 or not offs.is_contiguous() or offs.numel() != groups:
+            raise ValueError("offs must be a contiguous int32 CUDA tensor of `groups` elements")
+
+
+def mx_grouped_mm_fp4(a, b, a_scale, b_scale, c, offs, groups, M, N, K, out_dtype=None,
+                      stream=None) -> None:
+    """Grouped MXFP4 product (C ABI mx_grouped_mm_fp4): rows [offs[g-1], offs[g])
+    of a times b[g] (b is [groups][N][K/2]); offs is an int32 device tensor."""
+    _check_grouped(True, a, b, a_scale, b_scale, c, offs, groups, M, N, K)
+    st = _lib.mx_grouped_mm_fp4(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), _ptr(offs),
+                                groups, M, N, K, _out_code(c, out_dtype), _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_grouped_mm_fp4")
+
+
+def mx_grouped_mm_fp8(a, b, a_scale, b_scale, c, offs, groups, M, N, K, out_dtype=None,
+                      stream=None) -> None:
+    """Grouped MXFP8 product (C ABI mx_grouped_mm_fp8); b is [groups][N][K]."""
+    _check_grouped(False, a, b, a_scale, b_scale, c, offs, groups, M, N, K)
+    st = _lib.mx_grouped_mm_fp8(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), _ptr(offs),
+                                groups, M, N, K, _out_code(c, out_dtype), _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_grouped_mm_fp8")
+
+
+def mx_grouped_mm_config(is_fp4, a, b, a_scale, b_scale, c, offs, groups, M, N, K, variant,
+                         out_dtype=None, stream=None) -> None:
+    _check_grouped(bool(is_fp4), a, b, a_scale, b_scale, c, offs, groups, M, N, K)
+    st = _lib.mx_grouped_mm_config(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                   _ptr(c), _ptr(offs), groups, M, N, K, _out_code(c, out_dtype),
+                                   variant, _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_grouped_mm_config")
+
+
+def mx_grouped_num_variants() -> int:
+    return _lib.mx_grouped_num_variants()
+
+
+def mx_grouped_variant_name(variant) -> str | None:
+    n = _lib.mx_grouped_variant_name(variant)
+    return n.decode() if n is not None else None
+
+
+def mx_grouped_default_variant(groups, M, N) -> int:
+    return _lib.mx_grouped_default_variant(groups, M, N)
 
 
 # ------------------------------------------------------------- convenience

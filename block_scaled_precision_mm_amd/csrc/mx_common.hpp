@@ -68,6 +68,11 @@ struct GemmArgs {
     int nsteps;           // K / 128
     unsigned row_bytes;   // packed bytes per operand row: K/2 (FP4) or K (FP8)
     unsigned srow_bytes;  // scale bytes per row: K/32
+    // grouped products only (mx_group.hpp): end offset of each group's rows
+    // of A and C, and the group count; B and its scales hold one [N][K]
+    // operand per group
+    const int *offs;
+    int groups;
 };
 
 // Cache-policy bits of a buffer load on gfx950: 2 = non-temporal (stream).

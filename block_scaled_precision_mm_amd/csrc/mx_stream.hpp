@@ -36,6 +36,7 @@
 #pragma once
 
 #include "mx_common.hpp"
+#include "mx_group.hpp"
 
 namespace mxg {
 
@@ -107,7 +108,7 @@ __device__ __forceinline__ void stream_mfma_group(const StreamGroup<F, MT, WN> &
 
 // MT x WN 16x16 subtiles per workgroup, KW waves splitting K, D groups in
 // flight per wave.
-template <int F, int MT, int WN, int KW, int D, int OUT>
+template <int F, int MT, int WN, int KW, int D, int OUT, int GRP = 0>
 __global__ __launch_bounds__(64 * KW)
 void mx_gemm_stream(GemmArgs p)
 {
@@ -115,7 +116,15 @@ void mx_gemm_stream(GemmArgs p)
     const int lane = threadIdx.x & 63;
     const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
-    const int m0 = blockIdx.y * (16 * MT);
+    int m0 = blockIdx.y * (16 * MT);
+    if constexpr (GRP) {
+        // grouped product: a unit is one M tile (blockIdx.y) of some group
+        int grp, local, row0, rows;
+        if (!find_group(p.offs, p.groups, p.M, (int)blockIdx.y, 16 * MT, 1, grp, local, row0, rows))
+            return;
+        select_group<OUT>(p, grp, row0, rows);
+        m0 = local * (16 * MT);
+    }
     const int n0 = blockIdx.x * (16 * WN);
 
     // Buffers over this workgroup's rows only: rows past M or N fall

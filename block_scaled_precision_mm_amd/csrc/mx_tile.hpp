@@ -61,6 +61,7 @@
 
 #include <utility>
 
+#include "mx_group.hpp"
 #include "mx_lds.hpp"
 
 namespace mxg {
@@ -95,13 +96,17 @@ struct TileGeom {
     }
 };
 
+// Linear workgroup index -> position in tile order: workgroups b, b + 8,
+// b + 16, ... (one XCD) get consecutive positions.
+__device__ __forceinline__ int xcd_remap(int b, int total)
+{
+    return (total & 7) == 0 ? (b & 7) * (total >> 3) + (b >> 3) : b;
+}
+
 // Remap the linear workgroup index to an output tile (see "Tile order").
 __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int &tm, int &tn)
 {
-    const int total = nbm * nbn;
-    int pid = b;
-    if ((total & 7) == 0)
-        pid = (b & 7) * (total >> 3) + (b >> 3);
+    const int pid = xcd_remap(b, nbm * nbn);
     constexpr int GM = 8;
     const int per_group = GM * nbn;
     const int grp = pid / per_group;
@@ -178,7 +183,7 @@ struct TileRegs {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT>
+template <int F, int MT, int NT, int OUT, int GRP = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
@@ -191,9 +196,22 @@ void mx_gemm_tile(GemmArgs p)
     const int r = lane & 31, g = lane >> 5;
     const int wm = wave & 1, wn = wave >> 1;
 
-    const int nbm = (p.M + G::BM - 1) / G::BM, nbn = (p.N + G::BN - 1) / G::BN;
+    const int nbn = (p.N + G::BN - 1) / G::BN;
     int tm, tn;
-    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    if constexpr (GRP) {
+        // grouped product: a unit is one tile; a group's tiles in M-fastest
+        // order, so the workgroups of one XCD share the group's B columns
+        int grp, local, row0, rows;
+        if (!find_group(p.offs, p.groups, p.M, xcd_remap(blockIdx.x, gridDim.x), G::BM, nbn, grp,
+                        local, row0, rows))
+            return;
+        select_group<OUT>(p, grp, row0, rows);
+        const int nbm = (rows + G::BM - 1) / G::BM;
+        tm = local % nbm;
+        tn = local / nbm;
+    } else {
+        tile_of(blockIdx.x, (p.M + G::BM - 1) / G::BM, nbn, tm, tn);
+    }
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int mrows = min(G::BM, p.M - m0);
     const int nrows = min(G::BN, p.N - n0);

@@ -126,6 +126,29 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
+// Grouped products: the same kernels with the group lookup at the start.
+#define MXG_GSFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O, 1>)
+#define MXG_GSOUTS(F, MT, WN, KW) \
+    {MXG_GSFN(F, MT, WN, KW, OUT_BF16), MXG_GSFN(F, MT, WN, KW, OUT_F16), MXG_GSFN(F, MT, WN, KW, OUT_F32)}
+#define MXG_GSTREAM(MT, WN, KW)                                                       \
+    {"gstream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                       \
+     {MXG_GSOUTS(FMT_FP8, MT, WN, KW), MXG_GSOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0}
+#define MXG_GTFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O, 1>)
+#define MXG_GTOUTS(F, MT, NT) \
+    {MXG_GTFN(F, MT, NT, OUT_BF16), MXG_GTFN(F, MT, NT, OUT_F16), MXG_GTFN(F, MT, NT, OUT_F32)}
+#define MXG_GTILE(NAME, MT, NT)                                                     \
+    {NAME, 64 * (MT), 64 * (NT), 256,                                               \
+     {MXG_GTOUTS(FMT_FP8, MT, NT), MXG_GTOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1}
+
+const Variant kGroupVariants[] = {
+    MXG_GSTREAM(1, 2, 4),
+    MXG_GSTREAM(2, 4, 8),
+    MXG_GTILE("gtile_128x128", 2, 2),
+    MXG_GTILE("gtile_256x128", 4, 2),
+};
+constexpr int kNumGroupVariants = (int)(sizeof(kGroupVariants) / sizeof(kGroupVariants[0]));
+constexpr int64_t kMaxGroups = 1 << 16;
+
 // ---------------------------------------------------------------- validation
 // Largest K: every per-workgroup buffer range (at most 256 rows) must stay
 // below 2^31 bytes.
@@ -236,6 +259,8 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     p.nsteps = (int)(K / 128);
     p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
     p.srow_bytes = (unsigned)(K / 32);
+    p.offs = nullptr;
+    p.groups = 0;
     const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
     dim3 grid;
     if (v.linear) {
@@ -255,6 +280,113 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
         return MXG_ERR_HIP;
     }
     return MXG_OK;
+}
+
+// ------------------------------------------------------------ grouped
+int validate_grouped(const void *a, const void *b, const void *sa, const void *sb, const void *c,
+                     const int32_t *offs, int64_t groups, int64_t M, int64_t N, int64_t K,
+                     int out_dtype)
+{
+    if (!offs)
+        return MXG_ERR_NULL;
+    if (groups < 1 || groups > kMaxGroups || M < 0)
+        return MXG_ERR_SHAPE;
+    // M = 0 computes nothing but is checked like a one-row product, except
+    // that A, its scales and C (empty tensors) may be NULL
+    if (M == 0) {
+        a = a ? a : b;
+        sa = sa ? sa : sb;
+        c = c ? c : b;
+    }
+    int rc = validate(a, b, sa, sb, c, M > 0 ? M : 1, N, K, out_dtype);
+    if (rc)
+        return rc;
+    if ((uintptr_t)offs & 3u)
+        return MXG_ERR_PTR_ALIGN;
+    if (groups > INT64_MAX / N || groups * N > INT64_MAX / K)
+        return MXG_ERR_SHAPE;
+    return MXG_OK;
+}
+
+// Default grouped kernel from the mean rows per group.
+int pick_group_variant(int64_t groups, int64_t M, int64_t N)
+{
+    (void)N;
+    const int64_t mean = M / groups;
+    if (mean <= 16)
+        return 0;          // gstream_1x2_k4
+    if (mean <= 48)
+        return 1;          // gstream_2x4_k8
+    if (mean <= 256)
+        return 2;          // gtile_128x128
+    return 3;              // gtile_256x128
+}
+
+int launch_grouped(int is_fp4, const void *a, const void *b, const void *sa, const void *sb,
+                   void *c, const int32_t *offs, int64_t groups, int64_t M, int64_t N, int64_t K,
+                   int out_dtype, int variant, hipStream_t stream)
+{
+    const Variant &v = kGroupVariants[variant];
+    GemmArgs p;
+    p.a = (const uint8_t *)a;
+    p.b = (const uint8_t *)b;
+    p.sa = (const uint8_t *)sa;
+    p.sb = (const uint8_t *)sb;
+    p.c = c;
+    p.M = (int)M;                 // total rows; each workgroup narrows it to its group
+    p.N = (int)N;
+    p.nsteps = (int)(K / 128);
+    p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
+    p.srow_bytes = (unsigned)(K / 32);
+    p.offs = offs;
+    p.groups = (int)groups;
+    // worst case over all splits of M rows into the groups
+    const int64_t mtiles = cdiv(M, v.bm) + groups, gx = cdiv(N, v.bn);
+    dim3 grid;
+    if (v.linear) {
+        if (mtiles * gx > INT32_MAX)
+            return MXG_ERR_SHAPE;
+        grid = dim3((unsigned)(mtiles * gx));
+    } else {
+        if (gx > INT32_MAX || mtiles > 65535)
+            return MXG_ERR_SHAPE;
+        grid = dim3((unsigned)gx, (unsigned)mtiles);
+    }
+    hipLaunchKernelGGL(v.fn[is_fp4 ? 1 : 0][out_dtype], grid, dim3(v.threads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXG_ERR_HIP;
+    }
+    return MXG_OK;
+}
+
+// variant: an index into kGroupVariants, or kPickDefault.
+constexpr int kPickDefault = -1000;
+
+int run_grouped(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
+                const int32_t *offs, int64_t groups, int64_t M, int64_t N, int64_t K,
+                int out_dtype, int variant, hipStream_t stream)
+{
+    int rc = validate_grouped(a, b, sa, sb, c, offs, groups, M, N, K, out_dtype);
+    if (rc)
+        return rc;
+    if (variant == kPickDefault)
+        variant = pick_group_variant(groups, M, N);
+    if (variant < 0 || variant >= kNumGroupVariants)
+        return MXG_ERR_CONFIG;
+    if (M == 0)
+        return MXG_OK;
+    // the worst-case grid must fit the launch (checked again in launch_grouped)
+    const Variant &v = kGroupVariants[variant];
+    const int64_t mtiles = cdiv(M, v.bm) + groups, gx = cdiv(N, v.bn);
+    if (v.linear ? mtiles * gx > INT32_MAX : (gx > INT32_MAX || mtiles > 65535))
+        return MXG_ERR_SHAPE;
+    rc = check_device();
+    if (rc)
+        return rc;
+    return launch_grouped(is_fp4, a, b, sa, sb, c, offs, groups, M, N, K, out_dtype, variant,
+                          stream);
 }
 
 int run_default(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
@@ -376,6 +508,47 @@ int mx_quantize_bf16(const void *x, void *codes, void *scales, int64_t rows, int
         return MXG_ERR_HIP;
     }
     return MXG_OK;
+}
+
+int mx_grouped_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                      void *c, const int32_t *offs, int64_t groups, int64_t M, int64_t N,
+                      int64_t K, int out_dtype, mxg_stream_t stream)
+{
+    return run_grouped(1, a, b, a_scale, b_scale, c, offs, groups, M, N, K, out_dtype, kPickDefault,
+                       (hipStream_t)stream);
+}
+
+int mx_grouped_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                      void *c, const int32_t *offs, int64_t groups, int64_t M, int64_t N,
+                      int64_t K, int out_dtype, mxg_stream_t stream)
+{
+    return run_grouped(0, a, b, a_scale, b_scale, c, offs, groups, M, N, K, out_dtype, kPickDefault,
+                       (hipStream_t)stream);
+}
+
+int mx_grouped_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
+                         const void *b_scale, void *c, const int32_t *offs, int64_t groups,
+                         int64_t M, int64_t N, int64_t K, int out_dtype, int variant,
+                         mxg_stream_t stream)
+{
+    return run_grouped(is_fp4 ? 1 : 0, a, b, a_scale, b_scale, c, offs, groups, M, N, K,
+                       out_dtype, variant, (hipStream_t)stream);
+}
+
+int mx_grouped_num_variants(void) { return kNumGroupVariants; }
+
+const char *mx_grouped_variant_name(int variant)
+{
+    if (variant < 0 || variant >= kNumGroupVariants)
+        return nullptr;
+    return kGroupVariants[variant].name;
+}
+
+int mx_grouped_default_variant(int64_t groups, int64_t M, int64_t N)
+{
+    if (groups < 1 || groups > kMaxGroups || M < 0 || N < 1)
+        return MXG_ERR_SHAPE;
+    return pick_group_variant(groups, M, N);
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

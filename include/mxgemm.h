@@ -141,6 +141,54 @@ const char *mx_variant_name(int variant);
 int mx_quantize_bf16(const void *x, void *codes, void *scales, int64_t rows, int64_t K,
                      int is_fp4, mxg_stream_t stream);
 
+/*
+ * Grouped (mixture-of-experts) MX GEMM ("PyTorch 接上 FlyDSL", 5ulink.com:
+ * support-matrix row "Grouped GEMM" -- F.grouped_mm, the groups of A may
+ * differ in length and empty groups are skipped -- and "MXFP8 Grouped GEMM"
+ * among the next steps in the closing paragraph).  One call computes, for
+ * every group g with rows [offs[g-1], offs[g]) of A (offs[-1] = 0):
+ *
+ *   C[rows of g] = A[rows of g] * B[g]^T      (the MX product above)
+ *
+ * a        [M][K/2] (FP4) or [M][K] (FP8): all groups' rows, in group order.
+ * b        [groups][N][K/2] or [groups][N][K]: one NT operand per group.
+ * a_scale  [M][K/32];  b_scale [groups][N][K/32].
+ * c        [M][N] of out_dtype.  Rows in some group are overwritten; rows
+ *          past the last group's end are not written.
+ * offs     DEVICE memory, int32 [groups], 4-byte aligned: the end row of
+ *          each group (cumulative sizes).  Read by the kernels, so no host
+ *          synchronization is needed.  Entries are used as
+ *          end[g] = min(M, max(0, offs[0..g])), so any content yields
+ *          in-bounds rows; a group with end[g] == end[g-1] is empty and
+ *          costs nothing.
+ * groups   1 .. 65536.   M >= 0 (0: nothing is enqueued, and a, a_scale
+ *          and c may be NULL), N >= 1, K as for mx_scaled_mm_*.
+ *          groups * N * K must fit int64.
+ *
+ * Same alignment, ownership and error contract as mx_scaled_mm_fp4/fp8,
+ * plus MXG_ERR_NULL for a NULL offs and MXG_ERR_SHAPE for a group count
+ * out of range or a shape whose worst-case grid does not fit (rows per
+ * group are only known on the device, so the grid covers the worst split).
+ * Nothing is allocated.
+ */
+int mx_grouped_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                      void *c, const int32_t *offs, int64_t groups, int64_t M, int64_t N,
+                      int64_t K, int out_dtype, mxg_stream_t stream);
+int mx_grouped_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
+                      void *c, const int32_t *offs, int64_t groups, int64_t M, int64_t N,
+                      int64_t K, int out_dtype, mxg_stream_t stream);
+/* Grouped product with an explicit kernel variant, 0 .. mx_grouped_num_variants()-1
+ * (names from mx_grouped_variant_name); MXG_ERR_CONFIG for an unknown one. */
+int mx_grouped_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
+                         const void *b_scale, void *c, const int32_t *offs, int64_t groups,
+                         int64_t M, int64_t N, int64_t K, int out_dtype, int variant,
+                         mxg_stream_t stream);
+int mx_grouped_num_variants(void);
+const char *mx_grouped_variant_name(int variant);
+/* The variant mx_grouped_mm_fp4/fp8 pick (from the mean rows per group),
+ * or MXG_ERR_SHAPE. */
+int mx_grouped_default_variant(int64_t groups, int64_t M, int64_t N);
+
 /* The variant the default entry points pick for a shape (>= 0), or a
  * negative status for an invalid shape. */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
@@ -153,7 +201,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 3
+#define MXGEMM_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

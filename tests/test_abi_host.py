@@ -37,6 +37,11 @@ def lib():
     L.mx_variant_max_k.argtypes = [INT, INT]
     L.mx_variant_max_k.restype = I64
     L.mx_quantize_bf16.argtypes = [P, P, P, I64, I64, INT, P]
+    L.mx_grouped_mm_fp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, INT, P]
+    L.mx_grouped_mm_fp8.argtypes = L.mx_grouped_mm_fp4.argtypes
+    L.mx_grouped_mm_config.argtypes = [INT, P, P, P, P, P, P, I64, I64, I64, I64, INT, INT, P]
+    L.mx_grouped_variant_name.restype = ctypes.c_char_p
+    L.mx_grouped_default_variant.argtypes = [I64, I64, I64]
     return L
 
 
@@ -56,7 +61,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 3
+    assert lib.mx_abi_version() == 4
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -113,6 +118,47 @@ def test_invalid_arguments_rejected_before_any_hip_call(lib, fn, args, status):
 def test_quantize_invalid_arguments(lib, args, status):
     rc = lib.mx_quantize_bf16(*args, None)
     assert rc == status, (rc, lib.mx_status_string(rc))
+
+
+@pytest.mark.parametrize("fn", ["mx_grouped_mm_fp4", "mx_grouped_mm_fp8"])
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, A, A, 0, 4, 64, 8, 128, 0), -1),          # null offs
+    ((0, A, A, A, A, A, 4, 64, 8, 128, 0), -1),          # null a
+    ((A, A, A, A, A, A, 0, 64, 8, 128, 0), -2),          # no groups
+    ((A, A, A, A, A, A, (1 << 16) + 1, 64, 8, 128, 0), -2),   # too many groups
+    ((A, A, A, A, A, A, 4, -1, 8, 128, 0), -2),          # M < 0
+    ((A, A, A, A, A, A, 4, 64, 0, 128, 0), -2),          # N = 0
+    ((A, A, A, A, A, A, 4, 64, 8, 96, 0), -3),           # K % 128
+    ((A, A, A, A, A, A, 4, 0, 8, 96, 0), -3),            # M = 0 is still checked
+    ((A, A, A, A, A, A + 2, 4, 64, 8, 128, 0), -4),      # offs not 4-byte aligned
+    ((A, A, A, A, A + 8, A, 4, 64, 8, 128, 0), -4),      # c not 16-byte aligned
+    ((A, A, A, A, A, A, 4, 64, 8, 128, 7), -5),          # bad out dtype
+    ((A, A, A, A, A, A, 1 << 16, 64, (1 << 31) - 1, 1 << 22, 0), -2),   # groups*N*K beyond int64
+    ((A, A, A, A, A, A, 1 << 16, 1 << 30, 1 << 16, 128, 0), -2),      # worst-case grid too large
+])
+def test_grouped_invalid_arguments(lib, fn, args, status):
+    rc = getattr(lib, fn)(*args, None)
+    assert rc == status, (rc, lib.mx_status_string(rc))
+
+
+def test_grouped_configs(lib):
+    n = lib.mx_grouped_num_variants()
+    assert n >= 1
+    for v in range(n):
+        assert lib.mx_grouped_variant_name(v)
+    assert lib.mx_grouped_variant_name(n) is None
+    ok = (A, A, A, A, A, A, 4, 64, 64, 512, 0)
+    assert lib.mx_grouped_mm_config(1, *ok, -1, None) == -9
+    assert lib.mx_grouped_mm_config(0, *ok, n, None) == -9
+    # argument errors take precedence over the variant check
+    assert lib.mx_grouped_mm_config(1, A, A, A, A, A, 0, 4, 64, 64, 512, 0, 99, None) == -1
+    # M = 0 with valid arguments enqueues nothing (no HIP call, so it passes here)
+    assert lib.mx_grouped_mm_fp8(A, A, A, A, A, A, 4, 0, 64, 512, 0, None) == 0
+    assert lib.mx_grouped_mm_fp8(0, A, 0, A, 0, A, 4, 0, 64, 512, 0, None) == 0
+    assert lib.mx_grouped_mm_fp8(0, 0, 0, A, 0, A, 4, 0, 64, 512, 0, None) == -1
+    for shape in ((8, 8192, 4096), (32, 256, 2048), (64, 1, 7168), (1, 100000, 128)):
+        assert 0 <= lib.mx_grouped_default_variant(*shape) < n
+    assert lib.mx_grouped_default_variant(0, 8, 8) == -2
 
 
 def test_invalid_configs(lib):
