@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated operand sets (0 = one set, cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", type=int, default=None,
+                    help="grouped workloads: kernel variant index (default: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -49,20 +51,21 @@ def parse():
 
 
 KERNEL_HEADER = {"stream_": "mx_stream.hpp", "lds_": "mx_lds.hpp", "tile_": "mx_tile.hpp",
-                 "skinny_": "mx_skinny.hpp", "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp"}
+                 "skinny_": "mx_skinny.hpp", "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp",
+                 "gstream_": "mx_stream.hpp", "gtile_": "mx_tile.hpp"}
 
 
 def kernel_source_digest(kernel_name):
     """sha256 over the sources a kernel is built from (its header, the
-    headers that one includes, the variant table and the build flags):
-    counter-derived traffic figures are only reported for the kernels they
-    were measured on."""
+    headers that one includes, and the build flags; the variant's template
+    parameters are in its name): counter-derived traffic figures are only
+    reported for the kernels they were measured on."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "block_scaled_precision_mm_amd", "csrc")
     head = next((h for p, h in KERNEL_HEADER.items() if kernel_name.startswith(p)), None)
     if head is None:
-        return None
+        raise ValueError("no source mapping for kernel %r" % kernel_name)
     todo, seen = [head], set()
     while todo:
         name = todo.pop()
@@ -72,7 +75,7 @@ def kernel_source_digest(kernel_name):
         with open(os.path.join(csrc, name)) as f:
             todo += re.findall(r'#include "([^"/]+)"', f.read())
     files = [os.path.join(csrc, n) for n in sorted(seen)]
-    files += [os.path.join(csrc, "mxgemm.hip"), os.path.join(ROOT, "block_scaled_precision_mm_amd", "build.py")]
+    files.append(os.path.join(ROOT, "block_scaled_precision_mm_amd", "build.py"))
     h = hashlib.sha256()
     for path in files:
         with open(path, "rb") as f:
@@ -263,6 +266,122 @@ def bench_quant(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_grouped(gc, budget_s):
+    """The oracle, as it stands, on whole output rows of the largest group
+    (the grouped product is the plain one per group)."""
+    import oracle
+    oracle.build()
+    cores = host_threads()
+    g = int(gc.sizes.argmax())
+    r0 = int(gc.offs[g] - gc.sizes[g])
+    rb = gc.a.shape[1]
+    bg = gc.b.reshape(gc.G, gc.N, rb)[g]
+    sbg = gc.sb.reshape(gc.G, gc.N, -1)[g]
+    t0 = time.perf_counter()
+    oracle.gemm(gc.fmt, gc.a[r0:r0 + 1], bg, gc.sa[r0:r0 + 1], sbg, 1, gc.N, gc.K)
+    t_row = max(time.perf_counter() - t0, 1e-6)
+    n = int(max(1, min(int(gc.sizes[g]), budget_s / t_row)))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemm(gc.fmt, gc.a[r0:r0 + n], bg, gc.sa[r0:r0 + n], sbg, n, gc.N, gc.K)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n < gc.sizes[g]:
+            break
+    flops = 2.0 * n * gc.N * gc.K * reps
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of the %d rows of group %d (N=%d, K=%d) x %d repetitions, %.2f s"
+                      % (n, int(gc.sizes[g]), g, gc.N, gc.K, reps, dt)}
+
+
+def bench_grouped(args):
+    """One step = one grouped MX product (one launch) over all groups."""
+    import numpy as np
+    import torch
+
+    import mxgen
+    import block_scaled_precision_mm_amd as mx
+
+    torch.cuda.set_device(0)
+    gc = mxgen.grouped_case(args.workload)
+    is_fp4 = gc.fmt == "fp4"
+    dev = torch.device("cuda:0")
+    set_bytes = gc.a.nbytes + gc.b.nbytes + gc.sa.nbytes + gc.sb.nbytes + gc.M * gc.N * 2
+    R = 1 if args.rotate_bytes <= 0 else max(1, math.ceil(args.rotate_bytes / set_bytes))
+    R = min(R, 4096)
+    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (gc.a, gc.b, gc.sa, gc.sb)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+    outs = [torch.empty((gc.M, gc.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    offs = torch.from_numpy(gc.offs).to(dev)
+    variant = args.variant if args.variant is not None else mx.mx_grouped_default_variant(gc.G, gc.M, gc.N)
+    stream = torch.cuda.current_stream()
+    st_ptr = stream.cuda_stream
+    entry = mx._lib.mx_grouped_mm_config
+    ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
+            for s_, o in zip(sets, outs)]
+
+    def step(i):
+        a, b, sa, sb, c = ptrs[i % R]
+        rc = entry(1 if is_fp4 else 0, a, b, sa, sb, c, offs.data_ptr(), gc.G, gc.M, gc.N, gc.K, 0,
+                   variant, st_ptr)
+        if rc:
+            raise mx.MxGemmError(rc, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for _ in range(max(8, K // 4)):
+        filler.add_(1.0)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / K
+    del filler
+    flops = gc.flops
+    alg_bytes = gc.algorithmic_bytes(2)
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[gc.fmt] * 1e12)
+    name = mx.mx_grouped_variant_name(variant)
+    if t_hbm >= t_mfma:
+        ach = alg_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[gc.fmt],
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[gc.fmt], 4), "traffic": None}
+    roof.update({"kernel": name, "algorithmic_bytes": int(alg_bytes), "kernel_us": round(ms * 1e3, 3),
+                 "roofline_us": round(max(t_hbm, t_mfma) * 1e6, 3)})
+    rec = recorded_traffic(args.workload, name)
+    if rec is not None:
+        roof["traffic"] = rec["hbm_bytes_per_launch"]
+        roof["traffic_unit"] = "bytes/launch"
+        roof["traffic_vs_algorithmic"] = round(rec["hbm_bytes_per_launch"] / alg_bytes, 3)
+    out = {
+        "metric": "grouped MX GEMM TFLOPS on 1 MI355X and % of HBM/MFMA roofline",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4" if is_fp4 else "mxfp8", "data": "synthetic",
+        "config": {"workload": args.workload, "groups": gc.G, "M": gc.M, "N": gc.N, "K": gc.K,
+                   "recipe": gc.recipe, "rotating_sets": R, "variant": name, "out": "bf16"},
+        "roofline": roof,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_grouped(gc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -274,6 +393,9 @@ def main():
         return
     if args.workload.startswith("quant_"):
         bench_quant(args)
+        return
+    if args.workload.startswith("g"):
+        bench_grouped(args)
         return
     import numpy as np
     import torch

@@ -134,7 +134,7 @@ def test_quantize_invalid_arguments(lib, args, status):
     ((A, A, A, A, A + 8, A, 4, 64, 8, 128, 0), -4),      # c not 16-byte aligned
     ((A, A, A, A, A, A, 4, 64, 8, 128, 7), -5),          # bad out dtype
     ((A, A, A, A, A, A, 1 << 16, 64, (1 << 31) - 1, 1 << 22, 0), -2),   # groups*N*K beyond int64
-    ((A, A, A, A, A, A, 1 << 16, 1 << 30, 1 << 16, 128, 0), -2),      # worst-case grid too large
+    ((A, A, A, A, A, A, 1 << 16, (1 << 31) - 1, 1 << 16, 128, 0), -2),   # worst-case grid too large
 ])
 def test_grouped_invalid_arguments(lib, fn, args, status):
     rc = getattr(lib, fn)(*args, None)
