@@ -178,6 +178,47 @@ def grouped_gemm(fmt: str, a, b, sa, sb, offs, groups: int, M: int, N: int, K: i
     return c, s, covered
 
 
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+
+
+def activation(act: int, x):
+    """The epilogue activations in double precision, from their definitions:
+    ReLU max(x, 0); SiLU x * sigmoid(x) = x / (1 + e^-x); GELU with the tanh
+    form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, dtype=np.float64)
+    if act == ACT_NONE:
+        return x.copy()
+    if act == ACT_RELU:
+        return np.where(x > 0, x, 0.0)
+    with np.errstate(over="ignore"):
+        if act == ACT_SILU:
+            return x / (1.0 + np.exp(-x))
+        if act == ACT_GELU_TANH:
+            return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    raise ValueError("unknown activation %r" % act)
+
+
+def epilogue(c, bias_bf16, act: int):
+    """GEMM tail fusion (roadmap item "GEMM 尾部融合" of "PyTorch 接上 FlyDSL"):
+    per-column bias (BF16 bit patterns [N], or None) added to the exact
+    product, then the activation; double precision.  Returns (y, slope):
+    y and |d act / d x| at the pre-activation value (used to carry the
+    product's error bound through the activation)."""
+    x = np.asarray(c, dtype=np.float64)
+    if bias_bf16 is not None:
+        b = (np.asarray(bias_bf16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+        x = x + b.astype(np.float64)[None, :]
+    y = activation(act, x)
+    if act == ACT_NONE:
+        slope = np.ones_like(x)
+    elif act == ACT_RELU:
+        slope = (x > 0).astype(np.float64)
+    else:
+        # |act'| of SiLU and tanh-GELU stays below 1.13 everywhere
+        slope = np.full_like(x, 1.13)
+    return y, slope
+
+
 def round_bf16(x) -> np.ndarray:
     """float64 -> bf16 bit patterns (uint16), round-to-nearest-even, direct."""
     lib = _load()
