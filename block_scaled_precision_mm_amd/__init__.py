@@ -58,10 +58,14 @@ _lib.mx_grouped_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _P, _I64, _I64, 
 _lib.mx_grouped_variant_name.argtypes = [_INT]
 _lib.mx_grouped_variant_name.restype = ctypes.c_char_p
 _lib.mx_grouped_default_variant.argtypes = [_I64, _I64, _I64]
+_lib.mx_scaled_mm_fused.argtypes = [_INT, _P, _P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
+_lib.mx_fused_variant_name.argtypes = [_INT]
+_lib.mx_fused_variant_name.restype = ctypes.c_char_p
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
-           "mx_grouped_num_variants", "mx_grouped_default_variant"):
+           "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
+           "mx_fused_num_variants"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
@@ -69,7 +73,8 @@ EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
            "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
            "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
-           "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant")
+           "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant",
+           "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name")
 
 
 class MxGemmError(RuntimeError):
@@ -262,6 +267,43 @@ def mx_grouped_variant_name(variant) -> str | None:
 
 def mx_grouped_default_variant(groups, M, N) -> int:
     return _lib.mx_grouped_default_variant(groups, M, N)
+
+
+OUT_BF16, OUT_F16, OUT_F32, OUT_MXFP8, OUT_MXFP4 = 0, 1, 2, 3, 4
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
+
+
+def mx_scaled_mm_fused(is_fp4, a, b, a_scale, b_scale, bias, act, c, c_scale, M, N, K,
+                       out_kind=None, variant=-1, stream=None) -> None:
+    """MX GEMM with a fused epilogue (C ABI mx_scaled_mm_fused):
+    y = act(A B^T + bias) into c (BF16/FP16/FP32, the dtype of c unless
+    out_kind is given) or, with out_kind OUT_MXFP8 / OUT_MXFP4, MX codes into
+    c (uint8 [M][N] or [M][N/2]) and E8M0 codes into c_scale (uint8 [M][N/32]).
+    bias: bfloat16 [N] tensor or None.  Argument marshalling only."""
+    _check_tensors(bool(is_fp4), a, b, a_scale, b_scale, None, M, N, K)
+    if out_kind is None:
+        out_kind = _out_code(c, None)
+    if isinstance(bias, torch.Tensor):
+        if not bias.is_cuda or bias.dtype != torch.bfloat16 or not bias.is_contiguous() or bias.numel() != N:
+            raise ValueError("bias must be a contiguous bfloat16 CUDA tensor of N elements")
+    if isinstance(c, torch.Tensor):
+        n = M * N if out_kind in (OUT_BF16, OUT_F16, OUT_F32, OUT_MXFP8) else M * N // 2
+        if not c.is_cuda or not c.is_contiguous() or c.numel() != n:
+            raise ValueError("c must be a contiguous CUDA tensor of %d elements" % n)
+    st = _lib.mx_scaled_mm_fused(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                 _ptr(bias), act, _ptr(c), _ptr(c_scale), M, N, K, out_kind, variant,
+                                 _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_scaled_mm_fused")
+
+
+def mx_fused_num_variants() -> int:
+    return _lib.mx_fused_num_variants()
+
+
+def mx_fused_variant_name(variant) -> str | None:
+    n = _lib.mx_fused_variant_name(variant)
+    return n.decode() if n is not None else None
 
 
 # ------------------------------------------------------------- convenience

@@ -46,7 +46,9 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 
 enum { FMT_FP8 = 0, FMT_FP4 = 1 };
-enum { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2 };
+// Output kinds.  OUT_MX8 / OUT_MX4 (fused epilogue only): the BF16-rounded
+// result MX-quantized along N (E4M3 / E2M1 codes + one E8M0 per 32 columns).
+enum { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2, OUT_MX8 = 3, OUT_MX4 = 4 };
 
 template <int F> struct FmtTraits;
 template <> struct FmtTraits<FMT_FP8> {
@@ -73,6 +75,11 @@ struct GemmArgs {
     // operand per group
     const int *offs;
     int groups;
+    // fused epilogue only (mx_epilogue.hpp): per-column BF16 bias or null,
+    // activation code, and the E8M0 scale output of the MX output kinds
+    const uint16_t *bias;
+    int act;
+    uint8_t *c_scale;
 };
 
 // Cache-policy bits of a buffer load on gfx950: 2 = non-temporal (stream).

@@ -36,6 +36,7 @@
 #pragma once
 
 #include "mx_common.hpp"
+#include "mx_epilogue.hpp"
 #include "mx_group.hpp"
 
 namespace mxg {
@@ -108,11 +109,13 @@ __device__ __forceinline__ void stream_mfma_group(const StreamGroup<F, MT, WN> &
 
 // MT x WN 16x16 subtiles per workgroup, KW waves splitting K, D groups in
 // flight per wave.
-template <int F, int MT, int WN, int KW, int D, int OUT, int GRP = 0>
+template <int F, int MT, int WN, int KW, int D, int OUT, int GRP = 0, int EPI = 0>
 __global__ __launch_bounds__(64 * KW)
 void mx_gemm_stream(GemmArgs p)
 {
     static_assert(MT <= 4 && WN <= 4, "one lane per scale row: at most 64 rows per operand");
+    static_assert(!EPI || KW > 1, "the fused epilogue runs on the reduced tile");
+    static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
     const int lane = threadIdx.x & 63;
     const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int r = lane & 15, g = lane >> 4;
@@ -250,15 +253,53 @@ void mx_gemm_stream(GemmArgs p)
                 *reinterpret_cast<v4f *>(&red[kw][16 * x + r][16 * y + 4 * g]) = acc[x][y];
         __syncthreads();
         constexpr int NQ = 16 * MT * 4 * WN;   // float4 column groups in the tile
-        for (int q = threadIdx.x; q < NQ; q += 64 * KW) {
-            const int row = q / (4 * WN), c4 = q % (4 * WN);
-            v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
+        if constexpr (OUT == OUT_MX8 || OUT == OUT_MX4) {
+            // MX output: the 8 consecutive lanes of one row's 32-column block
+            // share its amax; N % 32 == 0, so a block is wholly inside or out
+            static_assert(WN % 2 == 0, "MX output needs whole 32-column blocks per workgroup");
+            constexpr int QF = OUT == OUT_MX4 ? FMT_FP4 : FMT_FP8;
+            for (int q0 = 0; q0 < NQ; q0 += 64 * KW) {
+                if (q0 + 64 * kw >= NQ)        // NQ is a multiple of 64: wave-uniform
+                    break;
+                const int q = q0 + (int)threadIdx.x;
+                const int row = q / (4 * WN), c4 = q % (4 * WN);
+                v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
 #pragma unroll
-            for (int w = 1; w < KW; ++w)
-                sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
-            const int m = m0 + row, n = n0 + 4 * c4;
-            if (m < p.M && n < p.N)
-                store4<OUT>(p.c, p.N, m, n, sum, vec_ok && n + 3 < p.N);
+                for (int w = 1; w < KW; ++w)
+                    sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
+                const int m = m0 + row, n = n0 + 4 * c4;
+                sum = epilogue4(sum, p, n);
+                const unsigned w2[2] = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+                unsigned amax = amax_pairs(w2);
+                amax = max(amax, (unsigned)__shfl_xor((int)amax, 1, 64));
+                amax = max(amax, (unsigned)__shfl_xor((int)amax, 2, 64));
+                amax = max(amax, (unsigned)__shfl_xor((int)amax, 4, 64));
+                const unsigned sc = block_scale_code<QF>(amax);
+                unsigned code[1];
+                mx_codes<QF, 2>(w2, sc, code);
+                if (m < p.M && n < p.N) {
+                    uint8_t *c8 = static_cast<uint8_t *>(p.c);
+                    if constexpr (QF == FMT_FP4)
+                        *reinterpret_cast<uint16_t *>(c8 + (size_t)m * (p.N / 2) + n / 2) = (uint16_t)code[0];
+                    else
+                        *reinterpret_cast<unsigned *>(c8 + (size_t)m * p.N + n) = code[0];
+                    if ((c4 & 7) == 0)
+                        p.c_scale[(size_t)m * (p.N / 32) + n / 32] = (uint8_t)sc;
+                }
+            }
+        } else {
+            for (int q = threadIdx.x; q < NQ; q += 64 * KW) {
+                const int row = q / (4 * WN), c4 = q % (4 * WN);
+                v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
+#pragma unroll
+                for (int w = 1; w < KW; ++w)
+                    sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
+                const int m = m0 + row, n = n0 + 4 * c4;
+                if constexpr (EPI)
+                    sum = epilogue4(sum, p, n);
+                if (m < p.M && n < p.N)
+                    store4<OUT>(p.c, p.N, m, n, sum, vec_ok && n + 3 < p.N);
+            }
         }
     }
 }

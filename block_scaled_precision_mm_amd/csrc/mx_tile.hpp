@@ -61,6 +61,7 @@
 
 #include <utility>
 
+#include "mx_epilogue.hpp"
 #include "mx_group.hpp"
 #include "mx_lds.hpp"
 
@@ -183,10 +184,11 @@ struct TileRegs {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT, int GRP = 0>
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
+    static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
     using G = TileGeom<F, MT, NT>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     __shared__ __attribute__((aligned(1024))) char smem[G::BYTES];
@@ -433,8 +435,10 @@ void mx_gemm_tile(GemmArgs p)
                 for (int v = 0; v < 4; ++v) {
                     const int n = n0 + wn * 32 * NT + 32 * j + 8 * v + 4 * g;
                     if (n < p.N) {
-                        const v4f q = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
-                                       acc[i][j][4 * v + 3]};
+                        v4f q = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
+                                 acc[i][j][4 * v + 3]};
+                        if constexpr (EPI)
+                            q = epilogue4(q, p, n);
                         store4<OUT>(p.c, p.N, m, n, q, vec_ok && n + 3 < p.N);
                     }
                 }
@@ -464,13 +468,17 @@ void mx_gemm_tile(GemmArgs p)
                 for (int j = 0; j < NT; ++j)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
+                        v4f y = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2],
+                                 acc[i][j][4 * v + 3]};
+                        if constexpr (EPI)
+                            y = epilogue4(y, p, n0 + wn * 32 * NT + 32 * j + 8 * v + 4 * g);
                         unsigned short h[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            if constexpr (OUT == OUT_BF16)
-                                h[e] = __builtin_bit_cast(unsigned short, (__bf16)acc[i][j][4 * v + e]);
-                            else
-                                h[e] = __builtin_bit_cast(unsigned short, (_Float16)acc[i][j][4 * v + e]);
+                            if constexpr (OUT == OUT_F16)
+                                h[e] = __builtin_bit_cast(unsigned short, (_Float16)y[e]);
+                            else   // BF16, and the BF16 rounding before MX quantization
+                                h[e] = __builtin_bit_cast(unsigned short, (__bf16)y[e]);
                         }
                         u2v w;
                         w.x = (unsigned)h[0] | ((unsigned)h[1] << 16);
@@ -485,7 +493,25 @@ void mx_gemm_tile(GemmArgs p)
                 const int row = k * RPI + lr;
                 const u4v q = *reinterpret_cast<const u4v *>(region + row * RS + 16 * lc);
                 const int m = m0 + wm * 32 * MT + hf * HR + row;
-                if (m < p.M) {
+                if constexpr (OUT == OUT_MX8 || OUT == OUT_MX4) {
+                    // the four consecutive lanes lc = 4b .. 4b+3 hold one
+                    // 32-column block of the row; N % 32 == 0, so a block is
+                    // wholly inside or outside
+                    constexpr int QF = OUT == OUT_MX4 ? FMT_FP4 : FMT_FP8;
+                    const unsigned w4[4] = {q[0], q[1], q[2], q[3]};
+                    const unsigned sc = block_scale_code<QF>(quad_max(amax_pairs(w4)));
+                    unsigned code[QF == FMT_FP4 ? 1 : 2];
+                    mx_codes<QF, 4>(w4, sc, code);
+                    if (m < p.M && ncol < p.N) {
+                        uint8_t *c8 = static_cast<uint8_t *>(p.c);
+                        if constexpr (QF == FMT_FP4)
+                            *reinterpret_cast<unsigned *>(c8 + (size_t)m * (p.N / 2) + ncol / 2) = code[0];
+                        else
+                            *reinterpret_cast<u2v *>(c8 + (size_t)m * p.N + ncol) = u2v{code[0], code[1]};
+                        if ((lc & 3) == 0)
+                            p.c_scale[(size_t)m * (p.N / 32) + ncol / 32] = (uint8_t)sc;
+                    }
+                } else if (m < p.M) {
                     unsigned short *dst = reinterpret_cast<unsigned short *>(p.c) + (size_t)m * p.N + ncol;
                     if (vec_ok) {
                         *reinterpret_cast<u4v *>(dst) = q;

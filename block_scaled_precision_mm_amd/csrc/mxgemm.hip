@@ -150,6 +150,39 @@ const Variant kGroupVariants[] = {
 constexpr int kNumGroupVariants = (int)(sizeof(kGroupVariants) / sizeof(kGroupVariants[0]));
 constexpr int64_t kMaxGroups = 1 << 16;
 
+// Fused-epilogue products: the same kernels with bias / activation and the
+// MX output kinds in the epilogue.
+struct FusedVariant {
+    const char *name;
+    int bm, bn;
+    int threads;
+    KernelFn fn[2][5];       // [fmt][out kind]
+    int linear;
+};
+#define MXG_FSFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O, 0, 1>)
+#define MXG_FSOUTS(F, MT, WN, KW)                                                                  \
+    {MXG_FSFN(F, MT, WN, KW, OUT_BF16), MXG_FSFN(F, MT, WN, KW, OUT_F16),                          \
+     MXG_FSFN(F, MT, WN, KW, OUT_F32), MXG_FSFN(F, MT, WN, KW, OUT_MX8), MXG_FSFN(F, MT, WN, KW, OUT_MX4)}
+#define MXG_FSTREAM(MT, WN, KW)                                                                    \
+    {"fstream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                                   \
+     {MXG_FSOUTS(FMT_FP8, MT, WN, KW), MXG_FSOUTS(FMT_FP4, MT, WN, KW)}, 0}
+#define MXG_FTFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O, 0, 1>)
+#define MXG_FTOUTS(F, MT, NT)                                                                      \
+    {MXG_FTFN(F, MT, NT, OUT_BF16), MXG_FTFN(F, MT, NT, OUT_F16), MXG_FTFN(F, MT, NT, OUT_F32),    \
+     MXG_FTFN(F, MT, NT, OUT_MX8), MXG_FTFN(F, MT, NT, OUT_MX4)}
+#define MXG_FTILE(NAME, MT, NT) \
+    {NAME, 64 * (MT), 64 * (NT), 256, {MXG_FTOUTS(FMT_FP8, MT, NT), MXG_FTOUTS(FMT_FP4, MT, NT)}, 1}
+
+const FusedVariant kFusedVariants[] = {
+    MXG_FSTREAM(1, 2, 4),
+    MXG_FSTREAM(2, 4, 8),
+    MXG_FTILE("ftile_128x128", 2, 2),
+    MXG_FTILE("ftile_256x128", 4, 2),
+    // (no 256x256 tile: with the epilogue's activation temporaries next to
+    // its 256 accumulators per lane it spills)
+};
+constexpr int kNumFusedVariants = (int)(sizeof(kFusedVariants) / sizeof(kFusedVariants[0]));
+
 // ---------------------------------------------------------------- validation
 // Largest K: every per-workgroup buffer range (at most 256 rows) must stay
 // below 2^31 bytes.
@@ -283,6 +316,10 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     return MXG_OK;
 }
 
+// variant argument of the run_* helpers: a table index, or this value for
+// the default choice
+constexpr int kPickDefault = -1000;
+
 // ------------------------------------------------------------ grouped
 int validate_grouped(const void *a, const void *b, const void *sa, const void *sb, const void *c,
                      const int32_t *offs, int64_t groups, int64_t M, int64_t N, int64_t K,
@@ -365,9 +402,6 @@ int launch_grouped(int is_fp4, const void *a, const void *b, const void *sa, con
     return MXG_OK;
 }
 
-// variant: an index into kGroupVariants, or kPickDefault.
-constexpr int kPickDefault = -1000;
-
 int run_grouped(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
                 const int32_t *offs, int64_t groups, int64_t M, int64_t N, int64_t K,
                 int out_dtype, int variant, hipStream_t stream)
@@ -391,6 +425,78 @@ int run_grouped(int is_fp4, const void *a, const void *b, const void *sa, const 
         return rc;
     return launch_grouped(is_fp4, a, b, sa, sb, c, offs, groups, M, N, K, out_dtype, variant,
                           stream);
+}
+
+// ------------------------------------------------------------ fused epilogue
+// Default fused kernel: the plain product's choice, among the kernels whose
+// workgroup tiles cover whole 32-column blocks.
+int pick_fused_variant(int64_t M, int64_t N)
+{
+    if (M <= 16)
+        return 0;          // fstream_1x2_k4
+    if (M <= 64)
+        return 1;          // fstream_2x4_k8
+    if (cdiv(M, 256) * cdiv(N, 128) >= 192)
+        return 3;          // ftile_256x128
+    return 2;              // ftile_128x128
+}
+
+int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const void *sb,
+              const void *bias, int act, void *c, void *c_scale, int64_t M, int64_t N, int64_t K,
+              int out_kind, int variant, hipStream_t stream)
+{
+    const bool mx_out = out_kind == MXG_OUT_MXFP8 || out_kind == MXG_OUT_MXFP4;
+    if (out_kind < MXG_OUT_BF16 || out_kind > MXG_OUT_MXFP4)
+        return MXG_ERR_DTYPE;
+    // operand checks as for the plain product (the output dtype is checked above)
+    int rc = validate(a, b, sa, sb, c, M, N, K, MXG_OUT_BF16);
+    if (rc)
+        return rc;
+    if (act < MXG_ACT_NONE || act > MXG_ACT_GELU_TANH)
+        return MXG_ERR_CONFIG;
+    if ((uintptr_t)bias & 1u)
+        return MXG_ERR_PTR_ALIGN;
+    if (mx_out) {
+        if (!c_scale)
+            return MXG_ERR_NULL;
+        if (N % 32)
+            return MXG_ERR_SHAPE;
+    }
+    if (variant == kPickDefault)
+        variant = pick_fused_variant(M, N);
+    if (variant < 0 || variant >= kNumFusedVariants)
+        return MXG_ERR_CONFIG;
+    const FusedVariant &v = kFusedVariants[variant];
+    const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
+    if (v.linear ? gx * gy > INT32_MAX : (gx > INT32_MAX || gy > 65535))
+        return MXG_ERR_SHAPE;
+    rc = check_device();
+    if (rc)
+        return rc;
+    GemmArgs p;
+    p.a = (const uint8_t *)a;
+    p.b = (const uint8_t *)b;
+    p.sa = (const uint8_t *)sa;
+    p.sb = (const uint8_t *)sb;
+    p.c = c;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.nsteps = (int)(K / 128);
+    p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
+    p.srow_bytes = (unsigned)(K / 32);
+    p.offs = nullptr;
+    p.groups = 0;
+    p.bias = (const uint16_t *)bias;
+    p.act = act;
+    p.c_scale = (uint8_t *)c_scale;
+    const dim3 grid = v.linear ? dim3((unsigned)(gx * gy)) : dim3((unsigned)gx, (unsigned)gy);
+    hipLaunchKernelGGL(v.fn[is_fp4 ? 1 : 0][out_kind], grid, dim3(v.threads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXG_ERR_HIP;
+    }
+    return MXG_OK;
 }
 
 int run_default(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
@@ -553,6 +659,24 @@ int mx_grouped_default_variant(int64_t groups, int64_t M, int64_t N)
     if (groups < 1 || groups > kMaxGroups || M < 0 || N < 1)
         return MXG_ERR_SHAPE;
     return pick_group_variant(groups, M, N);
+}
+
+int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_scale,
+                       const void *b_scale, const void *bias, int act, void *c, void *c_scale,
+                       int64_t M, int64_t N, int64_t K, int out_kind, int variant,
+                       mxg_stream_t stream)
+{
+    return run_fused(is_fp4 ? 1 : 0, a, b, a_scale, b_scale, bias, act, c, c_scale, M, N, K,
+                     out_kind, variant < 0 ? kPickDefault : variant, (hipStream_t)stream);
+}
+
+int mx_fused_num_variants(void) { return kNumFusedVariants; }
+
+const char *mx_fused_variant_name(int variant)
+{
+    if (variant < 0 || variant >= kNumFusedVariants)
+        return nullptr;
+    return kFusedVariants[variant].name;
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

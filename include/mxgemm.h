@@ -54,8 +54,19 @@ typedef struct ihipStream_t *mxg_stream_t;
 typedef enum {
     MXG_OUT_BF16 = 0, /* bfloat16, round to nearest even */
     MXG_OUT_F16 = 1,  /* IEEE half, round to nearest even */
-    MXG_OUT_F32 = 2   /* the FP32 accumulator before output rounding */
+    MXG_OUT_F32 = 2,  /* the FP32 accumulator before output rounding */
+    /* mx_scaled_mm_fused only: the BF16-rounded result MX-quantized along N */
+    MXG_OUT_MXFP8 = 3, /* E4M3 codes [M][N] + E8M0 [M][N/32] */
+    MXG_OUT_MXFP4 = 4  /* E2M1 codes [M][N/2] + E8M0 [M][N/32] */
 } mxg_out_t;
+
+/* Epilogue activations of mx_scaled_mm_fused. */
+typedef enum {
+    MXG_ACT_NONE = 0,
+    MXG_ACT_RELU = 1,      /* max(x, 0) */
+    MXG_ACT_SILU = 2,      /* x / (1 + exp(-x)) */
+    MXG_ACT_GELU_TANH = 3  /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+} mxg_act_t;
 
 typedef enum {
     MXG_OK = 0,
@@ -189,6 +200,40 @@ const char *mx_grouped_variant_name(int variant);
  * or MXG_ERR_SHAPE. */
 int mx_grouped_default_variant(int64_t groups, int64_t M, int64_t N);
 
+/*
+ * MX GEMM with a fused epilogue (the "GEMM 尾部融合" -- GEMM tail fusion --
+ * of the next steps in "PyTorch 接上 FlyDSL", 5ulink.com, closing
+ * paragraph; the pages do not define it further).  Per output element, in
+ * FP32 inside the kernel, before the output leaves it:
+ *
+ *   y[m][n] = act(C[m][n] + bias[n])          (C the product above)
+ *
+ * is_fp4      1: MXFP4 operands, 0: MXFP8; operands and scales as for
+ *             mx_scaled_mm_fp4/fp8.
+ * bias        BF16 [N] (2-byte aligned), or NULL for no bias.
+ * act         an mxg_act_t.
+ * out_kind    MXG_OUT_BF16 / F16 / F32: y rounded to nearest even into c
+ *             [M][N].  MXG_OUT_MXFP8 / MXFP4: y rounded to BF16, then
+ *             MX-quantized along N exactly as mx_quantize_bf16 quantizes a
+ *             BF16 [M][N] matrix: codes into c ([M][N] E4M3 or [M][N/2]
+ *             E2M1), E8M0 codes into c_scale [M][N/32]; needs N % 32 == 0.
+ *             The output is then the A operand of a following MX GEMM with
+ *             K' = N.
+ * c_scale     MX kinds only (else ignored, may be NULL).
+ * variant     negative: the library's choice; else 0 .. mx_fused_num_variants()-1.
+ *
+ * Errors as mx_scaled_mm_fp4/fp8, plus MXG_ERR_DTYPE for an unknown
+ * out_kind, MXG_ERR_CONFIG for an unknown act or variant, MXG_ERR_NULL for a
+ * missing c_scale, MXG_ERR_SHAPE for an MX kind with N % 32 != 0,
+ * MXG_ERR_PTR_ALIGN for an odd bias address.  Nothing is allocated.
+ */
+int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_scale,
+                       const void *b_scale, const void *bias, int act, void *c, void *c_scale,
+                       int64_t M, int64_t N, int64_t K, int out_kind, int variant,
+                       mxg_stream_t stream);
+int mx_fused_num_variants(void);
+const char *mx_fused_variant_name(int variant);
+
 /* The variant the default entry points pick for a shape (>= 0), or a
  * negative status for an invalid shape. */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
@@ -201,7 +246,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 4
+#define MXGEMM_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,8 @@ def lib():
     L.mx_grouped_mm_config.argtypes = [INT, P, P, P, P, P, P, I64, I64, I64, I64, INT, INT, P]
     L.mx_grouped_variant_name.restype = ctypes.c_char_p
     L.mx_grouped_default_variant.argtypes = [I64, I64, I64]
+    L.mx_scaled_mm_fused.argtypes = [INT, P, P, P, P, P, INT, P, P, I64, I64, I64, INT, INT, P]
+    L.mx_fused_variant_name.restype = ctypes.c_char_p
     return L
 
 
@@ -61,7 +63,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 4
+    assert lib.mx_abi_version() == 5
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -159,6 +161,24 @@ def test_grouped_configs(lib):
     for shape in ((8, 8192, 4096), (32, 256, 2048), (64, 1, 7168), (1, 100000, 128)):
         assert 0 <= lib.mx_grouped_default_variant(*shape) < n
     assert lib.mx_grouped_default_variant(0, 8, 8) == -2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 0, A, A, A, 0, 0, A, 0, 8, 64, 128, 0, -1), -1),     # null a
+    ((1, A, A, A, A, 0, 0, A, 0, 8, 64, 96, 0, -1), -3),      # K % 128
+    ((1, A, A, A, A, 0, 0, A, 0, 8, 64, 128, 5, -1), -5),     # unknown out kind
+    ((1, A, A, A, A, 0, 0, A, 0, 8, 64, 128, -1, -1), -5),
+    ((1, A, A, A, A, 0, 4, A, 0, 8, 64, 128, 0, -1), -9),     # unknown activation
+    ((1, A, A, A, A, A + 1, 0, A, 0, 8, 64, 128, 0, -1), -4), # odd bias address
+    ((1, A, A, A, A, 0, 0, A, 0, 8, 64, 128, 3, -1), -1),     # MX output without c_scale
+    ((0, A, A, A, A, 0, 0, A, A, 8, 48, 128, 4, -1), -2),     # MX output, N % 32
+    ((0, A, A, A, A, 0, 0, A, A, 8, 64, 128, 0, 99), -9),     # unknown variant
+])
+def test_fused_invalid_arguments(lib, args, status):
+    rc = lib.mx_scaled_mm_fused(*args, None)
+    assert rc == status, (rc, lib.mx_status_string(rc))
+    n = lib.mx_fused_num_variants()
+    assert n >= 1 and lib.mx_fused_variant_name(n) is None and lib.mx_fused_variant_name(0)
 
 
 def test_invalid_configs(lib):
