@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated operand sets (0 = one set, cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--epilogue", default=None, metavar="ACT,BIAS,OUT",
+                    help="time mx_scaled_mm_fused instead: activation none|relu|silu|gelu, "
+                         "bias 0|1, output bf16|mxfp8|mxfp4 (e.g. silu,1,mxfp4)")
     ap.add_argument("--variant", type=int, default=None,
                     help="grouped workloads: kernel variant index (default: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -420,12 +423,35 @@ def main():
     ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
             for s_, o in zip(sets, outs)]
     st_ptr = stream.cuda_stream
+    out_bytes = 2.0                 # bytes of C per output element
+    epi = None
+    if args.epilogue:
+        act_s, bias_s, out_s = args.epilogue.split(",")
+        act = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}[act_s]
+        out_kind = {"bf16": 0, "mxfp8": 3, "mxfp4": 4}[out_s]
+        bias = (torch.randn(cs.N, device=dev) * 4).to(torch.bfloat16) if bias_s == "1" else None
+        if out_kind >= 3:
+            out_bytes = (1.0 if out_kind == 3 else 0.5) + 1.0 / 32
+            c_scales = [torch.empty(cs.M * cs.N // 32, dtype=torch.uint8, device=dev) for _ in range(R)]
+        else:
+            c_scales = [None] * R
+        fused = mx._lib.mx_scaled_mm_fused
+        bias_ptr = bias.data_ptr() if bias is not None else None
+        csp = [t.data_ptr() if t is not None else None for t in c_scales]
+        epi = {"act": act_s, "bias": bias_s == "1", "out": out_s}
 
-    def step(i):
-        a, b, sa, sb, c = ptrs[i % R]
-        rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
-        if rc:
-            raise mx.MxGemmError(rc, "bench step")
+        def step(i):
+            a, b, sa, sb, c = ptrs[i % R]
+            rc = fused(1 if is_fp4 else 0, a, b, sa, sb, bias_ptr, act, c, csp[i % R], cs.M, cs.N, cs.K,
+                       out_kind, -1, st_ptr)
+            if rc:
+                raise mx.MxGemmError(rc, "bench step")
+    else:
+        def step(i):
+            a, b, sa, sb, c = ptrs[i % R]
+            rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
+            if rc:
+                raise mx.MxGemmError(rc, "bench step")
 
     for i in range(args.warmup):
         step(i)
@@ -455,7 +481,7 @@ def main():
     del filler
 
     flops = cs.flops
-    alg_bytes = cs.algorithmic_bytes(2)
+    alg_bytes = cs.algorithmic_bytes(2) - cs.M * cs.N * (2.0 - out_bytes)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_PEAK_TFLOPS[cs.fmt] * 1e12)
@@ -468,7 +494,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[cs.fmt],
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
     roof["kernel"] = mx.mx_variant_name(variant)
-    rec = recorded_traffic(args.workload, roof["kernel"])
+    if epi is not None:
+        roof["kernel"] = mx.mx_fused_variant_name(mx.mx_fused_default_variant(cs.M, cs.N))
+    rec = recorded_traffic(args.workload, roof["kernel"]) if epi is None else None
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]
         roof["traffic_unit"] = "bytes/launch"
@@ -493,7 +521,8 @@ def main():
         "config": {"workload": args.workload, "M": cs.M, "N": cs.N, "K": cs.K,
                    "operands": "MXFP4 (E2M1) + E8M0/32" if is_fp4 else "MXFP8 (E4M3) + E8M0/32",
                    "accumulate": "fp32", "out": "bf16", "layout": "NT", "recipe": cs.recipe,
-                   "rotating_sets": R, "variant": mx.mx_variant_name(variant)},
+                   "rotating_sets": R, "variant": roof["kernel"],
+                   "epilogue": epi},
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_s": round(t_enqueue, 4),

@@ -61,11 +61,12 @@ _lib.mx_grouped_default_variant.argtypes = [_I64, _I64, _I64]
 _lib.mx_scaled_mm_fused.argtypes = [_INT, _P, _P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
 _lib.mx_fused_variant_name.argtypes = [_INT]
 _lib.mx_fused_variant_name.restype = ctypes.c_char_p
+_lib.mx_fused_default_variant.argtypes = [_I64, _I64]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
-           "mx_fused_num_variants"):
+           "mx_fused_num_variants", "mx_fused_default_variant"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
@@ -74,7 +75,8 @@ EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
            "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant",
-           "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name")
+           "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name",
+           "mx_fused_default_variant")
 
 
 class MxGemmError(RuntimeError):
@@ -299,6 +301,10 @@ def mx_scaled_mm_fused(is_fp4, a, b, a_scale, b_scale, bias, act, c, c_scale, M,
 
 def mx_fused_num_variants() -> int:
     return _lib.mx_fused_num_variants()
+
+
+def mx_fused_default_variant(M, N) -> int:
+    return _lib.mx_fused_default_variant(M, N)
 
 
 def mx_fused_variant_name(variant) -> str | None:

@@ -7,7 +7,7 @@
 //
 // bias: BF16 [N] or absent; act: none, ReLU, SiLU x / (1 + e^-x), or GELU
 // in its tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), all in
-// FP32.  The output is y rounded to BF16 / FP16, y in FP32, or -- the MX
+// FP32 (hardware exp2 and reciprocal; see epilogue_value).  The output is y rounded to BF16 / FP16, y in FP32, or -- the MX
 // kinds -- y rounded to BF16 and then MX-quantized along N exactly as
 // mx_quantize_bf16 does it (so the output is the next GEMM's A operand,
 // K' = N): one E8M0 code per 32 consecutive columns from the block amax,
@@ -29,30 +29,44 @@ __device__ __forceinline__ float bf16_to_float(uint16_t h)
     return __uint_as_float((unsigned)h << 16);
 }
 
-__device__ __forceinline__ float epilogue_value(float x, int act)
+// e^-t as 2^(-t log2 e) on the hardware exp2 (v_exp_f32, about 1 ulp; the
+// rounding of the product adds a relative error of about |t| ulps, which
+// the activations below scale back down)
+__device__ __forceinline__ float exp_neg(float t)
 {
-    switch (act) {
-    case ACT_RELU:
-        return x > 0.f ? x : 0.f;
-    case ACT_SILU:
-        return x / (1.f + expf(-x));
-    case ACT_GELU_TANH:
-        return 0.5f * x * (1.f + tanhf(0.7978845608028654f * (x + 0.044715f * x * x * x)));
-    default:
-        return x;
-    }
+    return __builtin_amdgcn_exp2f(-1.4426950408889634f * t);
 }
 
-// Bias and activation on four consecutive columns n .. n+3 (columns past N
-// take no bias; their values are never stored).
+// The activations with the hardware exp2 and reciprocal (v_rcp_f32, 1 ulp):
+// a handful of instructions per element, so that the epilogue of a 4-wave
+// tile stays short next to its main loop.  Written from the definitions:
+//   SiLU(x) = x * 1 / (1 + e^-x)
+//   GELU(x) = 0.5 x (1 + tanh u) = x * 1 / (1 + e^-2u),  u = sqrt(2/pi) (x + 0.044715 x^3)
+// (1 + tanh u = 2 / (1 + e^-2u)).  For x -> -inf both reach -0 through
+// e^-t -> inf and rcp(inf) = 0; NaN stays NaN.
+// Branch-free (act is uniform; the selects cost less than control flow in
+// an unrolled epilogue, where branches around every element made the
+// register allocator spill the 256-accumulator tile).
+__device__ __forceinline__ float epilogue_value(float x, int act)
+{
+    const float relu = x > 0.f ? x : 0.f;
+    // SiLU: x * sigmoid(x); tanh-GELU: x * sigmoid(2u)
+    const float t = act == ACT_SILU ? x : 1.5957691216057308f * (x + 0.044715f * x * x * x);
+    const float gated = x * __builtin_amdgcn_rcpf(1.f + exp_neg(t));
+    return act == ACT_NONE ? x : (act == ACT_RELU ? relu : gated);
+}
+
+// Bias and activation on four consecutive columns n .. n+3.  The bias is
+// read through a buffer over [bias, bias + N) (empty when there is none):
+// columns past N, and every column without a bias, read 0 with no branch.
 __device__ __forceinline__ v4f epilogue4(v4f v, const GemmArgs &p, int n)
 {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias ? 2 * p.N : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float x = v[i];
-        if (p.bias && n + i < p.N)
-            x += bf16_to_float(p.bias[n + i]);
-        v[i] = epilogue_value(x, p.act);
+        const unsigned off = (unsigned)(n + i) * 2u;
+        const float b = bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(rb, off, 0, 0));
+        v[i] = epilogue_value(v[i] + b, p.act);
     }
     return v;
 }

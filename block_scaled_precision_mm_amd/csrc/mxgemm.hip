@@ -178,8 +178,7 @@ const FusedVariant kFusedVariants[] = {
     MXG_FSTREAM(2, 4, 8),
     MXG_FTILE("ftile_128x128", 2, 2),
     MXG_FTILE("ftile_256x128", 4, 2),
-    // (no 256x256 tile: with the epilogue's activation temporaries next to
-    // its 256 accumulators per lane it spills)
+    MXG_FTILE("ftile_256x256", 4, 4),
 };
 constexpr int kNumFusedVariants = (int)(sizeof(kFusedVariants) / sizeof(kFusedVariants[0]));
 
@@ -436,6 +435,8 @@ int pick_fused_variant(int64_t M, int64_t N)
         return 0;          // fstream_1x2_k4
     if (M <= 64)
         return 1;          // fstream_2x4_k8
+    if (cdiv(M, 256) * cdiv(N, 256) >= 384)
+        return 4;          // ftile_256x256
     if (cdiv(M, 256) * cdiv(N, 128) >= 192)
         return 3;          // ftile_256x128
     return 2;              // ftile_128x128
@@ -456,6 +457,8 @@ int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const vo
         return MXG_ERR_CONFIG;
     if ((uintptr_t)bias & 1u)
         return MXG_ERR_PTR_ALIGN;
+    if (bias && N > ((int64_t)1 << 30))   // the kernels read bias through a 2N-byte buffer range
+        return MXG_ERR_SHAPE;
     if (mx_out) {
         if (!c_scale)
             return MXG_ERR_NULL;
@@ -671,6 +674,13 @@ int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_s
 }
 
 int mx_fused_num_variants(void) { return kNumFusedVariants; }
+
+int mx_fused_default_variant(int64_t M, int64_t N)
+{
+    if (M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX)
+        return MXG_ERR_SHAPE;
+    return pick_fused_variant(M, N);
+}
 
 const char *mx_fused_variant_name(int variant)
 {

@@ -210,7 +210,7 @@ int mx_grouped_default_variant(int64_t groups, int64_t M, int64_t N);
  *
  * is_fp4      1: MXFP4 operands, 0: MXFP8; operands and scales as for
  *             mx_scaled_mm_fp4/fp8.
- * bias        BF16 [N] (2-byte aligned), or NULL for no bias.
+ * bias        BF16 [N] (2-byte aligned; N <= 2^30), or NULL for no bias.
  * act         an mxg_act_t.
  * out_kind    MXG_OUT_BF16 / F16 / F32: y rounded to nearest even into c
  *             [M][N].  MXG_OUT_MXFP8 / MXFP4: y rounded to BF16, then
@@ -233,6 +233,8 @@ int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_s
                        mxg_stream_t stream);
 int mx_fused_num_variants(void);
 const char *mx_fused_variant_name(int variant);
+/* The variant mx_scaled_mm_fused picks for variant < 0, or MXG_ERR_SHAPE. */
+int mx_fused_default_variant(int64_t M, int64_t N);
 
 /* The variant the default entry points pick for a shape (>= 0), or a
  * negative status for an invalid shape. */

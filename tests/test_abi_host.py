@@ -173,12 +173,17 @@ def test_grouped_configs(lib):
     ((1, A, A, A, A, 0, 0, A, 0, 8, 64, 128, 3, -1), -1),     # MX output without c_scale
     ((0, A, A, A, A, 0, 0, A, A, 8, 48, 128, 4, -1), -2),     # MX output, N % 32
     ((0, A, A, A, A, 0, 0, A, A, 8, 64, 128, 0, 99), -9),     # unknown variant
+    ((0, A, A, A, A, A, 0, A, A, 8, (1 << 30) + 32, 128, 0, -1), -2),   # bias beyond 2^30 columns
 ])
 def test_fused_invalid_arguments(lib, args, status):
     rc = lib.mx_scaled_mm_fused(*args, None)
     assert rc == status, (rc, lib.mx_status_string(rc))
     n = lib.mx_fused_num_variants()
     assert n >= 1 and lib.mx_fused_variant_name(n) is None and lib.mx_fused_variant_name(0)
+    lib.mx_fused_default_variant.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    for shape in ((1, 4096), (32, 14336), (64, 64), (256, 28672), (8192, 8192)):
+        assert 0 <= lib.mx_fused_default_variant(*shape) < n
+    assert lib.mx_fused_default_variant(0, 8) == -2
 
 
 def test_invalid_configs(lib):
