@@ -178,6 +178,31 @@ def grouped_gemm(fmt: str, a, b, sa, sb, offs, groups: int, M: int, N: int, K: i
     return c, s, covered
 
 
+def dense_values(dtype: str, bits, shape) -> np.ndarray:
+    """BF16 or FP16 bit patterns (uint16) -> float64 values, exactly."""
+    u = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).reshape(shape)
+    if dtype == "bf16":
+        return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return u.view(np.float16).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def dense_gemm(dtype: str, trans_a: int, trans_b: int, a_bits, b_bits, M: int, N: int, K: int):
+    """Dense BF16 / FP16 product C = A B ("PyTorch 接上 FlyDSL", support-matrix
+    row for torch.mm: FP16/BF16, static 2-D, NN / NT / TN / TT), in double.
+    A is stored [M][K] (trans_a 0) or [K][M] (trans_a 1); B is stored [K][N]
+    (trans_b 0) or [N][K] (trans_b 1).  Returns (c, s): float64 [M, N] and
+    sum_k |a_mk b_kn|.  A float64 matmul is exact here only up to double
+    rounding; products of BF16/FP16 values are exact in double and the sums
+    carry a relative error below K * 2^-53, far inside any GPU tolerance."""
+    A = dense_values(dtype, a_bits, (K, M) if trans_a else (M, K))
+    B = dense_values(dtype, b_bits, (N, K) if trans_b else (K, N))
+    A = A.T if trans_a else A
+    B = B.T if trans_b else B
+    return A @ B, np.abs(A) @ np.abs(B)
+
+
 ACT_NONE, ACT_RELU, ACT_SILU, ACT_GELU_TANH = 0, 1, 2, 3
 
 
