@@ -62,11 +62,12 @@ _lib.mx_scaled_mm_fused.argtypes = [_INT, _P, _P, _P, _P, _P, _INT, _P, _P, _I64
 _lib.mx_fused_variant_name.argtypes = [_INT]
 _lib.mx_fused_variant_name.restype = ctypes.c_char_p
 _lib.mx_fused_default_variant.argtypes = [_I64, _I64]
+_lib.mx_dense_gemm.argtypes = [_INT, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
-           "mx_fused_num_variants", "mx_fused_default_variant"):
+           "mx_fused_num_variants", "mx_fused_default_variant", "mx_dense_gemm"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
@@ -76,7 +77,7 @@ EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant",
            "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name",
-           "mx_fused_default_variant")
+           "mx_fused_default_variant", "mx_dense_gemm")
 
 
 class MxGemmError(RuntimeError):
@@ -310,6 +311,25 @@ def mx_fused_default_variant(M, N) -> int:
 def mx_fused_variant_name(variant) -> str | None:
     n = _lib.mx_fused_variant_name(variant)
     return n.decode() if n is not None else None
+
+
+def mx_dense_gemm(a, b, c, M, N, K, trans_a=0, trans_b=0, dtype=None, out_dtype=None,
+                  stream=None) -> None:
+    """Dense BF16 / FP16 product C = A B (C ABI mx_dense_gemm): a stored
+    [M][K] (trans_a 0) or [K][M] (1), b stored [K][N] (trans_b 0) or [N][K]
+    (1); dtype 0 BF16 / 1 FP16 (default: from a's torch dtype)."""
+    if dtype is None:
+        if not isinstance(a, torch.Tensor):
+            raise ValueError("dtype is required when a is a raw pointer")
+        dtype = {torch.bfloat16: 0, torch.float16: 1}[a.dtype]
+    for name, t, n in (("a", a, M * K), ("b", b, N * K), ("c", c, M * N)):
+        if isinstance(t, torch.Tensor):
+            if not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+                raise ValueError("%s must be a contiguous CUDA tensor of %d elements" % (name, n))
+    st = _lib.mx_dense_gemm(dtype, trans_a, trans_b, _ptr(a), _ptr(b), _ptr(c), M, N, K,
+                            _out_code(c, out_dtype), _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_dense_gemm")
 
 
 # ------------------------------------------------------------- convenience

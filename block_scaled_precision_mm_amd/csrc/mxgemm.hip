@@ -17,6 +17,7 @@
 
 #include "../../include/mxgemm.h"
 #include "mx_decode.hpp"
+#include "mx_dense.hpp"
 #include "mx_lds.hpp"
 #include "mx_quant.hpp"
 #include "mx_skinny.hpp"
@@ -502,6 +503,59 @@ int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const vo
     return MXG_OK;
 }
 
+// ------------------------------------------------------------ dense BF16 / FP16
+typedef void (*DenseFn)(DenseArgs);
+#define MXG_DFN4(T, TA, TB) \
+    {&mx_dense_gemm_kernel<T, TA, TB, OUT_BF16>, &mx_dense_gemm_kernel<T, TA, TB, OUT_F16>, \
+     &mx_dense_gemm_kernel<T, TA, TB, OUT_F32>}
+#define MXG_DLAYOUTS(T) {{MXG_DFN4(T, 0, 0), MXG_DFN4(T, 0, 1)}, {MXG_DFN4(T, 1, 0), MXG_DFN4(T, 1, 1)}}
+const DenseFn kDense[2][2][2][3] = {MXG_DLAYOUTS(DENSE_BF16), MXG_DLAYOUTS(DENSE_F16)};
+
+int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b, void *c,
+              int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream)
+{
+    if (!a || !b || !c)
+        return MXG_ERR_NULL;
+    if (dtype != 0 && dtype != 1)
+        return MXG_ERR_DTYPE;
+    if (out_dtype < MXG_OUT_BF16 || out_dtype > MXG_OUT_F32)
+        return MXG_ERR_DTYPE;
+    if (trans_a < 0 || trans_a > 1 || trans_b < 0 || trans_b > 1)
+        return MXG_ERR_CONFIG;
+    if (M < 1 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return MXG_ERR_SHAPE;
+    // every operand below 2 GiB (one buffer range each); C indexed in size_t
+    if (M * K >= ((int64_t)1 << 30) || N * K >= ((int64_t)1 << 30) || M > INT64_MAX / N)
+        return MXG_ERR_SHAPE;
+    // rows of both operands 16-byte aligned: the contiguous dimension % 8
+    const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
+    if (lda % 8 || ldb % 8)
+        return MXG_ERR_SHAPE;
+    if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
+        return MXG_ERR_PTR_ALIGN;
+    const int64_t gx = cdiv(N, DenseTile::BN), gy = cdiv(M, DenseTile::BM);
+    if (gx > INT32_MAX || gy > 65535)
+        return MXG_ERR_SHAPE;
+    int rc = check_device();
+    if (rc)
+        return rc;
+    DenseArgs p;
+    p.a = (const uint16_t *)a;
+    p.b = (const uint16_t *)b;
+    p.c = c;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    hipLaunchKernelGGL(kDense[dtype][trans_a][trans_b][out_dtype], dim3((unsigned)gx, (unsigned)gy),
+                       dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXG_ERR_HIP;
+    }
+    return MXG_OK;
+}
+
 int run_default(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
                 int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream)
 {
@@ -687,6 +741,12 @@ const char *mx_fused_variant_name(int variant)
     if (variant < 0 || variant >= kNumFusedVariants)
         return nullptr;
     return kFusedVariants[variant].name;
+}
+
+int mx_dense_gemm(int dtype, int trans_a, int trans_b, const void *a, const void *b, void *c,
+                  int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream)
+{
+    return run_dense(dtype, trans_a, trans_b, a, b, c, M, N, K, out_dtype, (hipStream_t)stream);
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

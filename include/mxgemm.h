@@ -236,6 +236,29 @@ const char *mx_fused_variant_name(int variant);
 /* The variant mx_scaled_mm_fused picks for variant < 0, or MXG_ERR_SHAPE. */
 int mx_fused_default_variant(int64_t M, int64_t N);
 
+/*
+ * Dense BF16 / FP16 GEMM ("PyTorch 接上 FlyDSL", 5ulink.com, support-matrix
+ * row for torch.mm: FP16/BF16, static 2-D, NN / NT / TN / TT):
+ *
+ *   C[M][N] = A[M][K] * B[K][N]      FP32 accumulation
+ *
+ * dtype      0: BF16 operands, 1: FP16 operands (bit patterns, 2 bytes each).
+ * trans_a    0: a is stored [M][K] row-major; 1: a is stored [K][M].
+ * trans_b    0: b is stored [K][N] row-major; 1: b is stored [N][K].
+ *            (trans_a = 0, trans_b = 1 is "NT", the MFMA's own layout.)
+ * c          [M][N] row-major of out_dtype (BF16 / FP16 / FP32), overwritten.
+ * M, N, K    >= 1; the contiguous dimension of each stored operand (K or M
+ *            for a, N or K for b) a multiple of 8; M*K and N*K below 2^30
+ *            elements.
+ *
+ * Returns MXG_OK after enqueueing, or MXG_ERR_NULL, MXG_ERR_DTYPE (dtype or
+ * out_dtype), MXG_ERR_CONFIG (trans flag not 0/1), MXG_ERR_SHAPE,
+ * MXG_ERR_PTR_ALIGN (a, b, c 16-byte aligned), MXG_ERR_DEVICE, MXG_ERR_HIP.
+ * Nothing is allocated; same ownership and stream contract as above.
+ */
+int mx_dense_gemm(int dtype, int trans_a, int trans_b, const void *a, const void *b, void *c,
+                  int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream);
+
 /* The variant the default entry points pick for a shape (>= 0), or a
  * negative status for an invalid shape. */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
@@ -248,7 +271,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 5
+#define MXGEMM_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

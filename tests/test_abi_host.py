@@ -63,7 +63,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 5
+    assert lib.mx_abi_version() == 6
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -184,6 +184,25 @@ def test_fused_invalid_arguments(lib, args, status):
     for shape in ((1, 4096), (32, 14336), (64, 64), (256, 28672), (8192, 8192)):
         assert 0 <= lib.mx_fused_default_variant(*shape) < n
     assert lib.mx_fused_default_variant(0, 8) == -2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 0, 0, A, A, 8, 8, 8, 0), -1),          # null a
+    ((2, 0, 0, A, A, A, 8, 8, 8, 0), -5),          # unknown dtype
+    ((0, 0, 0, A, A, A, 8, 8, 8, 3), -5),          # unknown out dtype
+    ((0, 2, 0, A, A, A, 8, 8, 8, 0), -9),          # trans flag
+    ((0, 0, 0, A, A, A, 0, 8, 8, 0), -2),          # M = 0
+    ((0, 0, 0, A, A, A, 8, 8, 12, 0), -2),         # a [M][K] rows not 16-byte aligned
+    ((0, 1, 0, A, A, A, 12, 8, 8, 0), -2),         # a [K][M] rows not 16-byte aligned
+    ((0, 0, 0, A, A, A, 8, 12, 8, 0), -2),         # b [K][N] rows not 16-byte aligned
+    ((0, 0, 1, A, A, A, 8, 8, 12, 0), -2),         # b [N][K] (and a) rows
+    ((0, 0, 0, A + 2, A, A, 8, 8, 8, 0), -4),      # a not 16-byte aligned
+    ((0, 0, 0, A, A, A, 1 << 16, 8, 1 << 14, 0), -2),   # operand beyond 2^30 elements
+])
+def test_dense_invalid_arguments(lib, args, status):
+    lib.mx_dense_gemm.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    rc = lib.mx_dense_gemm(*args, None)
+    assert rc == status, (rc, lib.mx_status_string(rc))
 
 
 def test_invalid_configs(lib):

@@ -1,0 +1,111 @@
+"""GPU parity of the dense BF16 / FP16 GEMM (mx_dense_gemm, through the C ABI)
+against the oracle's double-precision product, in the four layouts.
+
+Tolerance from the arithmetic: the products of two BF16 / FP16 values are
+exact in FP32, each MFMA adds 16 of them into the FP32 accumulator, and K/16
+such additions follow in sequence, so |c - c_ref| <= (K/16 + 16) 2^-24 S
+(S = sum |a b|) plus subnormal flushing.  16-bit output must be the
+round-to-nearest-even of the FP32 output bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mxgen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.fixture(scope="module")
+def mx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_scaled_precision_mm_amd as mx
+    return mx
+
+
+def bits(x, dtype):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(TDT[dtype]).view(torch.int16).numpy().view(np.uint16)
+
+
+def stored(X, trans):
+    return np.ascontiguousarray(X.T if trans else X)
+
+
+def run(mx, dtype, ta, tb, a_st, b_st, M, N, K, out):
+    a = torch.from_numpy(a_st.view(np.int16)).cuda().view(TDT[dtype])
+    b = torch.from_numpy(b_st.view(np.int16)).cuda().view(TDT[dtype])
+    c = torch.empty((M, N), dtype={"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out],
+                    device="cuda")
+    mx.mx_dense_gemm(a, b, c, M, N, K, ta, tb)
+    torch.cuda.synchronize()
+    if out == "f32":
+        return c.cpu().numpy().astype(np.float64)
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check(mx, dtype, ta, tb, M, N, K, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    A = bits(rng.standard_normal((M, K)) * scale, dtype)
+    B = bits(rng.standard_normal((K, N)) * scale, dtype)
+    a_st, b_st = stored(A, ta), stored(B, tb)
+    what = "%s %s%s %dx%dx%d" % (dtype, "NT"[ta], "NT"[tb], M, N, K)
+    print("dense", what, flush=True)
+    cref, S = oracle.dense_gemm(dtype, ta, tb, a_st, b_st, M, N, K)
+    c32 = run(mx, dtype, ta, tb, a_st, b_st, M, N, K, "f32")
+    tol = (K / 16 + 16) * 2.0 ** -24 * S + 2.0 ** -126 * K
+    err = np.abs(c32 - cref)
+    assert np.all(err <= tol), "%s: max err %g over tol (err/S %g)" % (what, (err - tol).max(), (err / np.maximum(S, 1e-300)).max())
+    for out, rnd in (("bf16", oracle.round_bf16), ("f16", oracle.round_f16)):
+        b16 = run(mx, dtype, ta, tb, a_st, b_st, M, N, K, out)
+        assert np.array_equal(b16, rnd(c32)), what + " " + out + " != RNE(f32)"
+
+
+LAYOUTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=["NN", "NT", "TN", "TT"])
+def test_layouts_small(mx, dtype, ta, tb):
+    # every contiguous dimension a multiple of 8; ragged against the 128 tile
+    # and the 32-deep stage; one stage, several stages, a K tail
+    for (M, N, K) in ((8, 8, 8), (136, 264, 40), (128, 128, 32), (264, 72, 520), (40, 1000, 1032)):
+        check(mx, dtype, ta, tb, M, N, K, seed=M + 3 * N + 7 * K + 11 * ta + 13 * tb)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ragged_rows(mx, dtype):
+    # M free when a is [M][K] (NN, NT); N free when b is [N][K] (NT, TT)
+    check(mx, dtype, 0, 1, 37, 45, 264, seed=1)
+    check(mx, dtype, 0, 0, 1, 64, 64, seed=2)
+    check(mx, dtype, 1, 1, 16, 3, 96, seed=3)
+
+
+def test_integer_valued_exact(mx):
+    # small integers: every partial sum exact in FP32, so the result is exact
+    rng = np.random.default_rng(5)
+    M, N, K = 192, 136, 1024
+    for ta, tb in LAYOUTS:
+        Ai = rng.integers(-8, 9, (M, K)).astype(np.float32)
+        Bi = rng.integers(-8, 9, (K, N)).astype(np.float32)
+        a_st, b_st = stored(bits(Ai, "bf16"), ta), stored(bits(Bi, "bf16"), tb)
+        c32 = run(mx, "bf16", ta, tb, a_st, b_st, M, N, K, "f32")
+        assert np.array_equal(c32, (Ai.astype(np.int64) @ Bi.astype(np.int64)).astype(np.float64))
+
+
+def test_large_sampled(mx):
+    # the bench shape, sampled outputs against the oracle
+    M = N = K = 2048
+    rng = np.random.default_rng(9)
+    A = bits(rng.standard_normal((M, K)), "bf16")
+    B = bits(rng.standard_normal((N, K)), "bf16")     # stored [N][K]: NT
+    c32 = run(mx, "bf16", 0, 1, A, B, M, N, K, "f32")
+    ms, ns = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+    Av = oracle.dense_values("bf16", A, (M, K))
+    Bv = oracle.dense_values("bf16", B, (N, K))
+    ref = np.einsum("ik,ik->i", Av[ms], Bv[ns])
+    S = np.einsum("ik,ik->i", np.abs(Av[ms]), np.abs(Bv[ns]))
+    assert np.all(np.abs(c32[ms, ns] - ref) <= (K / 16 + 16) * 2.0 ** -24 * S)
