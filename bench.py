@@ -385,6 +385,107 @@ def bench_grouped(args):
     print(json.dumps(out), flush=True)
 
 
+DENSE_PEAK_TFLOPS = 2500.0        # dense BF16 / FP16 MFMA
+
+
+def bench_dense(args):
+    """dense_<bf16|f16>_<nn|nt|tn|tt>_<M>x<N>x<K>: one mx_dense_gemm call per step."""
+    import numpy as np
+    import torch
+
+    import mxgen
+    import block_scaled_precision_mm_amd as mx
+
+    _, dt, lay, shape = args.workload.split("_")
+    M, N, K = (int(v) for v in shape.split("x"))
+    ta, tb = {"nn": (0, 0), "nt": (0, 1), "tn": (1, 0), "tt": (1, 1)}[lay]
+    dtype = {"bf16": 0, "f16": 1}[dt]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if dtype == 0 else torch.float16
+    # seeded N(0,1) draws (bf16-rounded, then cast for FP16), stored in the layout's order
+    xa = mxgen.normal_bf16(9001, (K, M) if ta else (M, K))
+    xb = mxgen.normal_bf16(9002, (N, K) if tb else (K, N))
+    a0 = torch.from_numpy(xa).to(dev).to(tdt)
+    b0 = torch.from_numpy(xb).to(dev).to(tdt)
+    set_bytes = (M * K + N * K + M * N) * 2
+    R = 1 if args.rotate_bytes <= 0 else max(1, math.ceil(args.rotate_bytes / set_bytes))
+    R = min(R, 4096)
+    sets = [(a0, b0)] + [(a0.clone(), b0.clone()) for _ in range(R - 1)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    st_ptr = stream.cuda_stream
+    ptrs = [(x.data_ptr(), y.data_ptr(), o.data_ptr()) for (x, y), o in zip(sets, outs)]
+
+    def step(i):
+        a, b, c = ptrs[i % R]
+        rc = mx._lib.mx_dense_gemm(dtype, ta, tb, a, b, c, M, N, K, 0, st_ptr)
+        if rc:
+            raise mx.MxGemmError(rc, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    steps = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for _ in range(max(8, steps // 4)):
+        filler.add_(1.0)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    del filler
+    flops = 2.0 * M * N * K
+    alg = float(set_bytes)
+    t_hbm = alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (DENSE_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        ach = alg / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / DENSE_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "dense_128x128_" + lay, "algorithmic_bytes": int(alg),
+                 "kernel_us": round(ms * 1e3, 3), "roofline_us": round(max(t_hbm, t_mfma) * 1e6, 3)})
+    out = {
+        "metric": "dense %s GEMM TFLOPS on 1 MI355X and %% of HBM/MFMA roofline" % dt.upper(),
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "layout": lay.upper(),
+                   "recipe": "bf16-rounded N(0,1), seeds 9001/9002", "rotating_sets": R, "out": "bf16"},
+        "roofline": roof,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        bits_a = (xa.view(np.uint32) >> 16).astype(np.uint16)
+        bits_b = (xb.view(np.uint32) >> 16).astype(np.uint16)
+        rows = max(1, min(M, 256))
+        t1 = time.perf_counter()
+        reps = 0
+        A = oracle.dense_values("bf16", bits_a, (K, M) if ta else (M, K))
+        A = (A.T if ta else A)[:rows]
+        while True:
+            oracle.dense_gemm("bf16", 0, tb, oracle.round_bf16(A), bits_b, rows, N, K)
+            reps += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        dt_s = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": 2.0 * rows * N * K * reps / dt_s / 1e12, "unit": "TFLOP/s",
+                               "cores": host_threads(), "kind": "oracle",
+                               "sample": "%d of %d rows x %d repetitions, %.2f s" % (rows, M, reps, dt_s)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -396,6 +497,9 @@ def main():
         return
     if args.workload.startswith("quant_"):
         bench_quant(args)
+        return
+    if args.workload.startswith("dense_"):
+        bench_dense(args)
         return
     if args.workload.startswith("g"):
         bench_grouped(args)
