@@ -8,16 +8,23 @@
 //     than the same rows cut into 64-byte slices read by different waves
 //     (split-K), and reading A once per workgroup instead of once per wave
 //     saves its share of the traffic;
-//   * L1: a 16-byte-per-lane load whose lanes follow the MFMA operand layout
-//     (16 rows in consecutive lanes) costs ~2.5x the address cycles of a
-//     coalesced one, and a one-row-per-lane scale load ~4x.
+//   * L1: a scale load with one row per lane (what a wave that owns a K
+//     slice of many rows needs) costs as much as all of a split-K kernel's
+//     MFMA and permute work together: at 32 x 14336 x 4096 E2M1, dropping
+//     those loads alone took a split-K stream kernel from 10.6 to 9.0 us.
+//     Here every scale byte is read once, in flat coalesced 16-byte pieces;
+//   * issue order: the A tile and the scale codes are requested first and
+//     are the only loads the workgroup waits for before its one barrier; the
+//     B ring is already in flight behind them, so HBM streams from the start.
+//     A ring of three 256-byte stages per wave (12 KB) beat deeper ones
+//     (four to eight stages) on MI355X, and non-temporal B loads (B is read
+//     once) gained about 1 us at 32 x 14336 x 4096.
 // So:
 //   * a workgroup of NW waves owns 16*NW consecutive B rows and all 16*MT A
 //     rows; wave w streams B rows [16w, 16w+16) over the whole of K -- no
 //     split-K, no reduction, no barrier in the K loop;
 //   * the A tile and the scale codes of all the workgroup's rows are loaded
-//     once, as flat coalesced ranges, into LDS (hence the K limit KMAX: the
-//     A tile must fit);
+//     once into LDS (hence the K limit KMAX: the A tile must fit);
 //   * B stages of 256 bytes per row are loaded with 16-byte loads in which
 //     16 consecutive lanes read one row's 256 contiguous bytes, into a
 //     G-deep register ring, stored into one of two private LDS slots and
@@ -31,7 +38,9 @@
 //
 // Ragged M / N: rows past the operand read as zeros (out of the buffer
 // range) and add exactly +0.  K tail: a B stage that runs past the row end
-// reads the next row's bytes, so MFMA steps past K are skipped.
+// reads the next row's bytes, so MFMA steps past K are skipped; a row's last
+// 16-byte scale piece may likewise run into the next row (or past the
+// buffer, reading zeros there), and only its dwords below K/128 are kept.
 #pragma once
 
 #include "mx_lds.hpp"
@@ -60,7 +69,10 @@ struct DecodeGeom {
     static constexpr int BYTES = B_OFF + NW * 2 * SLOT;
     // coalesced prologue loads per wave: A chunks (16 bytes), scale dwords
     static constexpr int PA = cdiv_c(BM * ACH, 64 * NW);
-    static constexpr int PS = cdiv_c((BM + BN) * NSTEP_MAX, 64 * NW);
+    // 16-byte scale pieces per row (4 steps each) and per wave
+    static constexpr int SQ_MAX = cdiv_c(NSTEP_MAX, 4);
+    static constexpr int PSA = cdiv_c(BM * SQ_MAX, 64 * NW);
+    static constexpr int PSB = cdiv_c(BN * SQ_MAX, 64 * NW);
     static_assert(BM % 8 == 0 && SW % SB == 0 && KMAX % 512 == 0, "tile geometry");
     static_assert(BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     __device__ static constexpr int a_off(int row, int c)
@@ -73,13 +85,28 @@ struct DecodeGeom {
     }
 };
 
+// Wait until at most `later` stages of LB loads each are outstanding.
+template <int LB, int G>
+__device__ __forceinline__ void wait_later(int later)
+{
+    if constexpr (G > 7) { if (later >= 7) { wait_vm<7 * LB>(); return; } }
+    if constexpr (G > 6) { if (later >= 6) { wait_vm<6 * LB>(); return; } }
+    if constexpr (G > 5) { if (later >= 5) { wait_vm<5 * LB>(); return; } }
+    if constexpr (G > 4) { if (later >= 4) { wait_vm<4 * LB>(); return; } }
+    if constexpr (G > 3) { if (later >= 3) { wait_vm<3 * LB>(); return; } }
+    if constexpr (G > 2) { if (later >= 2) { wait_vm<2 * LB>(); return; } }
+    if constexpr (G > 1) { if (later >= 1) { wait_vm<1 * LB>(); return; } }
+    wait_vm<0>();
+}
+
 template <int F, int MT, int NW, int KMAX, int G, int OUT>
 __global__ __launch_bounds__(64 * NW)
 void mx_gemm_decode(GemmArgs p)
 {
     using D = DecodeGeom<F, MT, NW, KMAX>;
-    constexpr int LB = 4;   // B loads per stage: 4 rows x 256 bytes each
-    static_assert(G >= 2 && G * LB + D::PA + 2 * D::PS < 64, "outstanding loads must fit the vmcnt field");
+    constexpr int LB = 4;
+    constexpr int PSA = D::PSA, PSB = D::PSB;
+    static_assert(G * LB + D::PA + PSA + PSB < 64, "outstanding loads must fit the vmcnt field");
     __shared__ __attribute__((aligned(1024))) char smem[D::BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -90,31 +117,94 @@ void mx_gemm_decode(GemmArgs p)
     const int nrows = min(D::BN, p.N - n0);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * p.row_bytes, mrows * p.row_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * p.row_bytes, nrows * p.row_bytes);
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
-    const int T = (int)((p.row_bytes + D::SW - 1) / D::SW);   // B stages
-    const int nst = p.nsteps;                                 // 128-K steps (<= NSTEP_MAX)
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
+    const int T = (int)((p.row_bytes + D::SW - 1) / D::SW);
+    const int nst = p.nsteps;
 
-    // ---- B ring: load j of a stage covers rows 4j .. 4j+3 of this wave's 16
-    // (lane l: row 4j + l/16, bytes 16*(l%16) of the stage's 256)
+    // prologue: the A tile (flat: chunk i is bytes [16i, 16i+16) of rows m0..,
+    // i.e. row i / CH, chunk i % CH) and the scale pieces (piece c is row
+    // c / CQ, steps 4 (c % CQ) ..) first, then the first G B stages
+    const unsigned CH = p.row_bytes / 16u;            // A chunks per row
+    const unsigned CQ = ((unsigned)nst + 3u) / 4u;    // 16-byte scale pieces per row
+    const unsigned a_chunks = (unsigned)mrows * CH;
+    const unsigned sa_chunks = (unsigned)mrows * CQ, sb_chunks = (unsigned)nrows * CQ;
+    // x / d as a multiply-high by ceil(2^32 / d) (exact for x < 2^32 / d, far
+    // above any index here); d = 1 has no 32-bit multiplier
+    const unsigned mch = 0xFFFFFFFFu / CH + 1u, mcq = 0xFFFFFFFFu / CQ + 1u;
+    auto row_of_piece = [&](unsigned c) { return CQ == 1u ? c : __umulhi(c, mcq); };
+    u4v av[D::PA], sva[PSA], svb[PSB];
+#pragma unroll
+    for (int i = 0; i < D::PA; ++i) {
+        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        av[i] = load16<CPOL_NONE>(ra, idx < a_chunks ? 16u * idx : kOutOfRange);
+    }
+#pragma unroll
+    for (int i = 0; i < PSA; ++i) {
+        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned row = row_of_piece(c);
+        sva[i] = load16<CPOL_NONE>(rsa, c < sa_chunks ? row * p.srow_bytes + 16u * (c - row * CQ) : kOutOfRange);
+    }
+#pragma unroll
+    for (int i = 0; i < PSB; ++i) {
+        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned row = row_of_piece(c);
+        svb[i] = load16<CPOL_NONE>(rsb, c < sb_chunks ? row * p.srow_bytes + 16u * (c - row * CQ) : kOutOfRange);
+    }
+
     const unsigned bload = (unsigned)(16 * wave + (lane >> 4)) * p.row_bytes + 16u * (unsigned)(lane & 15);
     const unsigned bstride = 4u * p.row_bytes;
     u4v stg[G][LB];
+    // stages past K read zeros but are issued all the same, so that the
+    // outstanding-load counts below are exact
     auto fill_stage = [&](u4v (&set)[LB], int t) {
-        if (t < T) {
+        const unsigned kt = t < T ? (unsigned)t * D::SW : kOutOfRange;
 #pragma unroll
-            for (int j = 0; j < LB; ++j)
-                set[j] = load16<CPOL_NONE>(rb, bload + (unsigned)j * bstride + (unsigned)t * D::SW);
-        } else {
-#pragma unroll
-            for (int j = 0; j < LB; ++j)
-                set[j] = u4v{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < LB; ++j)
+            set[j] = load16<CPOL_NT>(rb, bload + (unsigned)j * bstride + kt);
     };
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        fill_stage(stg[i], i);
+
+    wait_vm<G * LB>();   // the A tile and the scale pieces have landed
+#pragma unroll
+    for (int i = 0; i < D::PA; ++i) {
+        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        if (idx < a_chunks) {
+            const unsigned row = __umulhi(idx, mch), c = idx - row * CH;
+            *reinterpret_cast<u4v *>(smem + D::a_off((int)row, (int)c)) = av[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PSA; ++i) {
+        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        if (c < sa_chunks) {
+            const unsigned row = row_of_piece(c), k = 4u * (c - row * CQ);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < (unsigned)nst)
+                    *reinterpret_cast<unsigned *>(smem + D::SA_OFF + 4 * ((k + e) * D::BM + row)) = sva[i][e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PSB; ++i) {
+        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        if (c < sb_chunks) {
+            const unsigned row = row_of_piece(c), k = 4u * (c - row * CQ);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k + e < (unsigned)nst)
+                    *reinterpret_cast<unsigned *>(smem + D::SBS_OFF + 4 * ((k + e) * D::BN + row)) = svb[i][e];
+        }
+    }
+    __syncthreads();   // the A tile and scale codes are shared by all waves
+
+    // ---- B ring: load j of a stage covers rows 4j .. 4j+3 of this wave's 16
+    // (lane l: row 4j + l/16, bytes 16*(l%16) of the stage's 256), read once,
+    // so non-temporal
     char *slots = smem + D::B_OFF + wave * 2 * D::SLOT;
-    const int bw_lane = D::b_off(lane >> 4, lane & 15);   // row l/16 of a 4-row load, chunk l%16
+    const int bw_lane = D::b_off(lane >> 4, lane & 15);
     auto store_stage = [&](const u4v (&set)[LB], int t) {
         char *slot = slots + (t & 1) * D::SLOT;
 #pragma unroll
@@ -122,76 +212,24 @@ void mx_gemm_decode(GemmArgs p)
             *reinterpret_cast<u4v *>(slot + bw_lane + D::b_off(4 * j, 0)) = set[j];
     };
 
-    // ---- prologue: the first G B stages, then the A tile (flat: chunk i of
-    // the tile is bytes [16i, 16i+16) of rows m0.., i.e. row i / CH, chunk
-    // i % CH) and the scale dwords (flat: dword f of [A rows | B rows] is
-    // row f / NS, step f % NS), all in flight together
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-        fill_stage(stg[i], i);
-    const unsigned CH = p.row_bytes / 16u;             // A chunks per row
-    const unsigned NS = (unsigned)nst;                  // scale dwords per row
-    const unsigned a_chunks = (unsigned)mrows * CH;
-    const unsigned s_dwords = (unsigned)(mrows + nrows) * NS;
-    u4v av[D::PA];
-    unsigned sv[D::PS];
-#pragma unroll
-    for (int i = 0; i < D::PA; ++i) {
-        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
-        av[i] = load16<CPOL_NONE>(ra, idx < a_chunks ? 16u * idx : kOutOfRange);
-    }
-#pragma unroll
-    for (int i = 0; i < D::PS; ++i) {
-        const unsigned f = (unsigned)(64 * (NW * i + wave) + lane);
-        const unsigned fa = (unsigned)mrows * NS;       // A dwords come first
-        const bool isa = f < fa;
-        const unsigned off = f < s_dwords ? 4u * (isa ? f : f - fa) : kOutOfRange;
-        // one load may span A's and B's scale rows; a buffer resource must
-        // be uniform, so load from both with the other side's lanes out of
-        // range (they read 0)
-        sv[i] = load4(rsa, isa ? off : kOutOfRange) | load4(rsb, isa ? kOutOfRange : off);
-    }
-    wait_vm<0>();
-#pragma unroll
-    for (int i = 0; i < D::PA; ++i) {
-        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
-        if (idx < a_chunks) {
-            const unsigned row = idx / CH, c = idx % CH;
-            *reinterpret_cast<u4v *>(smem + D::a_off((int)row, (int)c)) = av[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < D::PS; ++i) {
-        const unsigned f = (unsigned)(64 * (NW * i + wave) + lane);
-        const unsigned fa = (unsigned)mrows * NS;
-        if (f < s_dwords) {
-            const bool isa = f < fa;
-            const unsigned ff = isa ? f : f - fa;
-            const unsigned row = ff / NS, k = ff % NS;
-            *reinterpret_cast<unsigned *>(smem + (isa ? D::SA_OFF + 4 * (k * D::BM + row)
-                                                      : D::SBS_OFF + 4 * (k * D::BN + row))) = sv[i];
-        }
-    }
-    __syncthreads();   // the A tile and scale codes are shared by all waves
-
     v4f acc[MT];
 #pragma unroll
     for (int x = 0; x < MT; ++x)
         acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // one stage: store it, refill its staging set, then its MFMA steps
+    // one stage: wait for its loads (the stages issued after it may stay in
+    // flight: the prologue issued G, each earlier stage refilled one below
+    // T), store it, refill its staging set, then its MFMA steps
     auto stage = [&](auto uc, int t) {
         constexpr int u = decltype(uc)::value;
-        if (t + G - 1 < T)
-            wait_vm<(G - 1) * LB>();   // stage t's loads (the G-1 later stages may be in flight)
-        else
-            wait_vm<0>();
+        wait_later<LB, G>(min(t + G, max(G, T)) - t - 1);
         store_stage(stg[u], t);
-        fill_stage(stg[u], t + G);
+        if (t + G < T)
+            fill_stage(stg[u], t + G);
         const char *slot = slots + (t & 1) * D::SLOT;
 #pragma unroll
         for (int s = 0; s < D::SPS; ++s) {
-            const int k = t * D::SPS + s;   // global step
+            const int k = t * D::SPS + s;
             if (k >= nst)
                 break;
             StepFrag<F> fb, fa[MT];
@@ -224,7 +262,6 @@ void mx_gemm_decode(GemmArgs p)
             if (t0 + decltype(uc)::value < T)
                 stage(uc, t0 + decltype(uc)::value);
         });
-    wait_vm<0>();
 
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
