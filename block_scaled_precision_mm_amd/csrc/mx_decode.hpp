@@ -20,9 +20,13 @@
 //     (four to eight stages) on MI355X, and non-temporal B loads (B is read
 //     once) gained about 1 us at 32 x 14336 x 4096.
 // So:
-//   * a workgroup of NW waves owns 16*NW consecutive B rows and all 16*MT A
-//     rows; wave w streams B rows [16w, 16w+16) over the whole of K -- no
-//     split-K, no reduction, no barrier in the K loop;
+//   * a workgroup owns 16*NW consecutive B rows and all 16*MT A rows; each
+//     16-row group of B is streamed by KS waves, wave (w, q) taking rows
+//     [16w, 16w+16) over the q-th of KS equal runs of K -- no barrier in the
+//     K loop; with KS > 1 the KS partial tiles are summed in LDS at the end,
+//     in part order.  Two waves per row group with two-stage rings streamed
+//     32 x 14336 x 4096 faster than one wave with three (a pure read of the
+//     same bytes in that pattern: 6.3 against 7.3 us);
 //   * the A tile and the scale codes of all the workgroup's rows are loaded
 //     once into LDS (hence the K limit KMAX: the A tile must fit);
 //   * B stages of 256 bytes per row are loaded with 16-byte loads in which
@@ -48,8 +52,9 @@
 
 namespace mxg {
 
-template <int F, int MT, int NW, int KMAX>
+template <int F, int MT, int NW, int KMAX, int KS = 1>
 struct DecodeGeom {
+    static constexpr int NWT = NW * KS;                      // waves: NW row groups x KS K parts
     static constexpr int SB = FmtTraits<F>::step_bytes;      // bytes per row per 128-K step
     static constexpr int BM = 16 * MT;                       // A rows
     static constexpr int BN = 16 * NW;                       // B rows (16 per wave)
@@ -65,14 +70,21 @@ struct DecodeGeom {
     // LDS map
     static constexpr int SA_OFF = BM / 8 * AGROUP;                         // [step][BM] dwords
     static constexpr int SBS_OFF = SA_OFF + NSTEP_MAX * BM * 4;            // [step][BN] dwords
-    static constexpr int B_OFF = SBS_OFF + NSTEP_MAX * BN * 4;             // [wave][2] slots
-    static constexpr int BYTES = B_OFF + NW * 2 * SLOT;
-    // coalesced prologue loads per wave: A chunks (16 bytes), scale dwords
-    static constexpr int PA = cdiv_c(BM * ACH, 64 * NW);
+    // B slots per wave: two with one wave per row group; one when KS waves
+    // share a row group (a wave's LDS operations run in order, so its next
+    // stage's stores cannot overtake the reads of the current one)
+    static constexpr int SLOTS = KS == 1 ? 2 : 1;
+    static constexpr int B_OFF = SBS_OFF + NSTEP_MAX * BN * 4;             // [wave][SLOTS] slots
+    static constexpr int BYTES = B_OFF + NWT * SLOTS * SLOT;
+    // coalesced prologue loads per wave: A chunks (16 bytes)
+    static constexpr int PA = cdiv_c(BM * ACH, 64 * NWT);
     // 16-byte scale pieces per row (4 steps each) and per wave
     static constexpr int SQ_MAX = cdiv_c(NSTEP_MAX, 4);
-    static constexpr int PSA = cdiv_c(BM * SQ_MAX, 64 * NW);
-    static constexpr int PSB = cdiv_c(BN * SQ_MAX, 64 * NW);
+    static constexpr int PSA = cdiv_c(BM * SQ_MAX, 64 * NWT);
+    static constexpr int PSB = cdiv_c(BN * SQ_MAX, 64 * NWT);
+    // partial tiles of the K parts past the first, summed at the end (in
+    // the A region, free by then)
+    static_assert((KS - 1) * NW * MT * 64 * 16 <= SA_OFF, "partials must fit the A region");
     static_assert(BM % 8 == 0 && SW % SB == 0 && KMAX % 512 == 0, "tile geometry");
     static_assert(BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     __device__ static constexpr int a_off(int row, int c)
@@ -99,11 +111,12 @@ __device__ __forceinline__ void wait_later(int later)
     wait_vm<0>();
 }
 
-template <int F, int MT, int NW, int KMAX, int G, int OUT>
-__global__ __launch_bounds__(64 * NW)
+template <int F, int MT, int NW, int KMAX, int G, int OUT, int KS = 1>
+__global__ __launch_bounds__(64 * NW * KS)
 void mx_gemm_decode(GemmArgs p)
 {
-    using D = DecodeGeom<F, MT, NW, KMAX>;
+    using D = DecodeGeom<F, MT, NW, KMAX, KS>;
+    constexpr int NWT = D::NWT;
     constexpr int LB = 4;
     constexpr int PSA = D::PSA, PSB = D::PSB;
     static_assert(G * LB + D::PA + PSA + PSB < 64, "outstanding loads must fit the vmcnt field");
@@ -111,6 +124,7 @@ void mx_gemm_decode(GemmArgs p)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rw = wave % NW, kh = wave / NW;   // row group, K part
     const int r = lane & 15, g = lane >> 4;
     const int m0 = blockIdx.y * D::BM, n0 = blockIdx.x * D::BN;
     const int mrows = min(D::BM, p.M - m0);
@@ -121,6 +135,8 @@ void mx_gemm_decode(GemmArgs p)
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
     const int T = (int)((p.row_bytes + D::SW - 1) / D::SW);
     const int nst = p.nsteps;
+    // this wave's stages [t0, t0 + nt) of the row group's T
+    const int t0 = kh * T / KS, nt = (kh + 1) * T / KS - t0;
 
     // prologue: the A tile (flat: chunk i is bytes [16i, 16i+16) of rows m0..,
     // i.e. row i / CH, chunk i % CH) and the scale pieces (piece c is row
@@ -136,29 +152,29 @@ void mx_gemm_decode(GemmArgs p)
     u4v av[D::PA], sva[PSA], svb[PSB];
 #pragma unroll
     for (int i = 0; i < D::PA; ++i) {
-        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned idx = (unsigned)(64 * (NWT * i + wave) + lane);
         av[i] = load16<CPOL_NONE>(ra, idx < a_chunks ? 16u * idx : kOutOfRange);
     }
 #pragma unroll
     for (int i = 0; i < PSA; ++i) {
-        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned c = (unsigned)(64 * (NWT * i + wave) + lane);
         const unsigned row = row_of_piece(c);
         sva[i] = load16<CPOL_NONE>(rsa, c < sa_chunks ? row * p.srow_bytes + 16u * (c - row * CQ) : kOutOfRange);
     }
 #pragma unroll
     for (int i = 0; i < PSB; ++i) {
-        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned c = (unsigned)(64 * (NWT * i + wave) + lane);
         const unsigned row = row_of_piece(c);
         svb[i] = load16<CPOL_NONE>(rsb, c < sb_chunks ? row * p.srow_bytes + 16u * (c - row * CQ) : kOutOfRange);
     }
 
-    const unsigned bload = (unsigned)(16 * wave + (lane >> 4)) * p.row_bytes + 16u * (unsigned)(lane & 15);
+    const unsigned bload = (unsigned)(16 * rw + (lane >> 4)) * p.row_bytes + 16u * (unsigned)(lane & 15);
     const unsigned bstride = 4u * p.row_bytes;
     u4v stg[G][LB];
     // stages past K read zeros but are issued all the same, so that the
     // outstanding-load counts below are exact
-    auto fill_stage = [&](u4v (&set)[LB], int t) {
-        const unsigned kt = t < T ? (unsigned)t * D::SW : kOutOfRange;
+    auto fill_stage = [&](u4v (&set)[LB], int i) {   // the wave's i-th stage
+        const unsigned kt = i < nt ? (unsigned)(t0 + i) * D::SW : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < LB; ++j)
             set[j] = load16<CPOL_NT>(rb, bload + (unsigned)j * bstride + kt);
@@ -170,7 +186,7 @@ void mx_gemm_decode(GemmArgs p)
     wait_vm<G * LB>();   // the A tile and the scale pieces have landed
 #pragma unroll
     for (int i = 0; i < D::PA; ++i) {
-        const unsigned idx = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned idx = (unsigned)(64 * (NWT * i + wave) + lane);
         if (idx < a_chunks) {
             const unsigned row = __umulhi(idx, mch), c = idx - row * CH;
             *reinterpret_cast<u4v *>(smem + D::a_off((int)row, (int)c)) = av[i];
@@ -178,7 +194,7 @@ void mx_gemm_decode(GemmArgs p)
     }
 #pragma unroll
     for (int i = 0; i < PSA; ++i) {
-        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned c = (unsigned)(64 * (NWT * i + wave) + lane);
         if (c < sa_chunks) {
             const unsigned row = row_of_piece(c), k = 4u * (c - row * CQ);
 #pragma unroll
@@ -189,7 +205,7 @@ void mx_gemm_decode(GemmArgs p)
     }
 #pragma unroll
     for (int i = 0; i < PSB; ++i) {
-        const unsigned c = (unsigned)(64 * (NW * i + wave) + lane);
+        const unsigned c = (unsigned)(64 * (NWT * i + wave) + lane);
         if (c < sb_chunks) {
             const unsigned row = row_of_piece(c), k = 4u * (c - row * CQ);
 #pragma unroll
@@ -203,10 +219,10 @@ void mx_gemm_decode(GemmArgs p)
     // ---- B ring: load j of a stage covers rows 4j .. 4j+3 of this wave's 16
     // (lane l: row 4j + l/16, bytes 16*(l%16) of the stage's 256), read once,
     // so non-temporal
-    char *slots = smem + D::B_OFF + wave * 2 * D::SLOT;
+    char *slots = smem + D::B_OFF + wave * D::SLOTS * D::SLOT;
     const int bw_lane = D::b_off(lane >> 4, lane & 15);
-    auto store_stage = [&](const u4v (&set)[LB], int t) {
-        char *slot = slots + (t & 1) * D::SLOT;
+    auto store_stage = [&](const u4v (&set)[LB], int i) {
+        char *slot = slots + (D::SLOTS == 2 ? (i & 1) * D::SLOT : 0);
 #pragma unroll
         for (int j = 0; j < LB; ++j)
             *reinterpret_cast<u4v *>(slot + bw_lane + D::b_off(4 * j, 0)) = set[j];
@@ -217,16 +233,18 @@ void mx_gemm_decode(GemmArgs p)
     for (int x = 0; x < MT; ++x)
         acc[x] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // one stage: wait for its loads (the stages issued after it may stay in
-    // flight: the prologue issued G, each earlier stage refilled one below
-    // T), store it, refill its staging set, then its MFMA steps
-    auto stage = [&](auto uc, int t) {
+    // one stage (the wave's i-th): wait for its loads (the stages issued
+    // after it may stay in flight: the prologue issued G, each earlier stage
+    // refilled one below nt), store it, refill its staging set, then its
+    // MFMA steps
+    auto stage = [&](auto uc, int i) {
         constexpr int u = decltype(uc)::value;
-        wait_later<LB, G>(min(t + G, max(G, T)) - t - 1);
-        store_stage(stg[u], t);
-        if (t + G < T)
-            fill_stage(stg[u], t + G);
-        const char *slot = slots + (t & 1) * D::SLOT;
+        wait_later<LB, G>(min(i + G, max(G, nt)) - i - 1);
+        store_stage(stg[u], i);
+        if (i + G < nt)
+            fill_stage(stg[u], i + G);
+        const char *slot = slots + (D::SLOTS == 2 ? (i & 1) * D::SLOT : 0);
+        const int t = t0 + i;
 #pragma unroll
         for (int s = 0; s < D::SPS; ++s) {
             const int k = t * D::SPS + s;
@@ -239,7 +257,7 @@ void mx_gemm_decode(GemmArgs p)
                 fb.d[0] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + g));
                 fb.d[1] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + 4 + g));
             }
-            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::BN + 16 * wave + r)) >> (8 * g);
+            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::BN + 16 * rw + r)) >> (8 * g);
             unsigned sa[MT];
 #pragma unroll
             for (int x = 0; x < MT; ++x) {
@@ -257,17 +275,38 @@ void mx_gemm_decode(GemmArgs p)
                 acc[x] = mfma<F>(fb, sb, fa[x], sa[x], acc[x]);
         }
     };
-    for (int t0 = 0; t0 < T; t0 += G)
+    for (int i0 = 0; i0 < nt; i0 += G)
         static_for<G>([&](auto uc) {
-            if (t0 + decltype(uc)::value < T)
-                stage(uc, t0 + decltype(uc)::value);
+            if (i0 + decltype(uc)::value < nt)
+                stage(uc, i0 + decltype(uc)::value);
         });
+
+    if constexpr (KS > 1) {
+        // the K parts past the first park their partial tiles in the A
+        // region; the first part's wave adds them in part order (fixed, so
+        // the result is deterministic)
+        v4f *part = reinterpret_cast<v4f *>(smem);
+        __syncthreads();   // every wave is done reading the A tile
+        if (kh > 0) {
+#pragma unroll
+            for (int x = 0; x < MT; ++x)
+                part[(((kh - 1) * NW + rw) * MT + x) * 64 + lane] = acc[x];
+        }
+        __syncthreads();
+        if (kh > 0)
+            return;
+#pragma unroll
+        for (int q = 1; q < KS; ++q)
+#pragma unroll
+            for (int x = 0; x < MT; ++x)
+                acc[x] += part[(((q - 1) * NW + rw) * MT + x) * 64 + lane];
+    }
 
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int x = 0; x < MT; ++x) {
         const int m = m0 + 16 * x + r;
-        const int n = n0 + 16 * wave + 4 * g;
+        const int n = n0 + 16 * rw + 4 * g;
         if (m < p.M && n < p.N)
             store4<OUT>(p.c, p.N, m, n, acc[x], vec_ok && n + 3 < p.N);
     }

@@ -68,15 +68,15 @@ constexpr int ring_depth(int fmt, int mt, int wn)
      {MXG_LOUTS(FMT_FP8, KW, WM, WN, MT, NT, S8, T8), MXG_LOUTS(FMT_FP4, KW, WM, WN, MT, NT, S4, T4)}, {0, 0}}
 
 // Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
-// (K up to K8 / K4 for FP8 / FP4), NW waves of NT B subtiles each streaming
-// through private rings of D stages of S8 / S4 steps.
-#define MXG_DFN(F, MT, NW, KM, G, O) (&mx_gemm_decode<F, MT, NW, KM, G, O>)
-#define MXG_DOUTS(F, MT, NW, KM, G)                                                        \
-    {MXG_DFN(F, MT, NW, KM, G, OUT_BF16), MXG_DFN(F, MT, NW, KM, G, OUT_F16),                \
-     MXG_DFN(F, MT, NW, KM, G, OUT_F32)}
-#define MXG_DECODE(NAME, MT, NW, G, K4, K8)                                                \
-    {NAME, 16 * (MT), 16 * (NW), 64 * (NW),                                                \
-     {MXG_DOUTS(FMT_FP8, MT, NW, K8, G), MXG_DOUTS(FMT_FP4, MT, NW, K4, G)}, {K8, K4}, 0}
+// (K up to K8 / K4 for FP8 / FP4), NW groups of 16 B rows, each streamed by
+// KS waves (one K part each) through private rings of G 256-byte stages.
+#define MXG_DFN(F, MT, NW, KM, G, O, KS) (&mx_gemm_decode<F, MT, NW, KM, G, O, KS>)
+#define MXG_DOUTS(F, MT, NW, KM, G, KS)                                                    \
+    {MXG_DFN(F, MT, NW, KM, G, OUT_BF16, KS), MXG_DFN(F, MT, NW, KM, G, OUT_F16, KS),        \
+     MXG_DFN(F, MT, NW, KM, G, OUT_F32, KS)}
+#define MXG_DECODE(NAME, MT, NW, G, KS, K4, K8)                                            \
+    {NAME, 16 * (MT), 16 * (NW), 64 * (NW) * (KS),                                         \
+     {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS)}, {K8, K4}, 0}
 
 // Decode-width tiles on the 32x32x64 instruction: waves split K, each
 // streams its run through a private register ring and LDS slot.
@@ -113,9 +113,11 @@ const Variant kVariants[] = {
     MXG_LDS("lds_32x64_w4",        1, 1, 4, 2, 1, 4, 2, 4, 4),
     MXG_LDS("lds_64x16_k4",        4, 1, 1, 4, 1, 2, 1, 3, 3),
     MXG_LDS("lds_32x32_k4",        4, 1, 1, 2, 2, 2, 1, 3, 3),
-    //          name              MT NW NT S4 S8 D  K4    K8
-    MXG_DECODE("decode_32x64",    2, 4, 3, 4096, 2048),
-    MXG_DECODE("decode_16x64",    1, 4, 3, 4096, 2048),
+    //          name              MT NW G  KS K4    K8
+    MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048),
+    MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048),
+    MXG_DECODE("decode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
+    MXG_DECODE("decode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
 
     MXG_SKINNY("skinny_32x64_k4",   1, 2, 4, 4),
     MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
@@ -262,10 +264,11 @@ int find_variant(const char *name)
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     // E2M1, 5-32 rows, wide N, A tile fits LDS: the whole-row decode kernel
-    // (32 x 14336 x 4096: 9.3 us against 10.6 for stream_2x4_k8; 16 rows:
-    // 8.2 against 9.2); at 1-4 rows the narrow stream tile is faster
+    // with two waves per row group (32 x 14336 x 4096: 9.2 us against 9.8
+    // with one wave and 10.6 for stream_2x4_k8; 16 rows: 8.4 against 9.4
+    // for stream_1x1_k4); at 1-4 rows the narrow stream tile is faster
     if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= 4096)
-        return find_variant(M <= 16 ? "decode_16x64" : "decode_32x64");
+        return find_variant(M <= 16 ? "decode_16x64_k2" : "decode_32x64_k2");
     if (M <= 16)
         return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
     if (M <= 32)
