@@ -599,7 +599,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
     roof["kernel"] = mx.mx_variant_name(variant)
     if epi is not None:
-        roof["kernel"] = mx.mx_fused_variant_name(mx.mx_fused_default_variant(cs.M, cs.N))
+        roof["kernel"] = mx.mx_fused_variant_name(mx.mx_fused_default_variant(is_fp4, cs.M, cs.N, cs.K))
     rec = recorded_traffic(args.workload, roof["kernel"]) if epi is None else None
     if rec is not None:
         roof["traffic"] = rec["hbm_bytes_per_launch"]

@@ -61,7 +61,9 @@ _lib.mx_grouped_default_variant.argtypes = [_I64, _I64, _I64]
 _lib.mx_scaled_mm_fused.argtypes = [_INT, _P, _P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
 _lib.mx_fused_variant_name.argtypes = [_INT]
 _lib.mx_fused_variant_name.restype = ctypes.c_char_p
-_lib.mx_fused_default_variant.argtypes = [_I64, _I64]
+_lib.mx_fused_default_variant.argtypes = [_INT, _I64, _I64, _I64]
+_lib.mx_fused_variant_max_k.argtypes = [_INT, _INT]
+_lib.mx_fused_variant_max_k.restype = _I64
 _lib.mx_dense_gemm.argtypes = [_INT, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
@@ -77,7 +79,7 @@ EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant",
            "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name",
-           "mx_fused_default_variant", "mx_dense_gemm")
+           "mx_fused_default_variant", "mx_fused_variant_max_k", "mx_dense_gemm")
 
 
 class MxGemmError(RuntimeError):
@@ -304,8 +306,15 @@ def mx_fused_num_variants() -> int:
     return _lib.mx_fused_num_variants()
 
 
-def mx_fused_default_variant(M, N) -> int:
-    return _lib.mx_fused_default_variant(M, N)
+def mx_fused_default_variant(is_fp4, M, N, K) -> int:
+    return _lib.mx_fused_default_variant(int(bool(is_fp4)), M, N, K)
+
+
+def mx_fused_variant_max_k(variant, is_fp4) -> int:
+    v = _lib.mx_fused_variant_max_k(variant, int(bool(is_fp4)))
+    if v < 0:
+        raise MxGemmError(v, "mx_fused_variant_max_k")
+    return v
 
 
 def mx_fused_variant_name(variant) -> str | None:

@@ -47,6 +47,7 @@
 // buffer, reading zeros there), and only its dwords below K/128 are kept.
 #pragma once
 
+#include "mx_epilogue.hpp"
 #include "mx_lds.hpp"
 #include "mx_tile.hpp"
 
@@ -111,12 +112,15 @@ __device__ __forceinline__ void wait_later(int later)
     wait_vm<0>();
 }
 
-template <int F, int MT, int NW, int KMAX, int G, int OUT, int KS = 1>
+// EPI: the fused epilogue (bias, activation, and the MX output kinds) on
+// the final tile, which then goes through LDS.
+template <int F, int MT, int NW, int KMAX, int G, int OUT, int KS = 1, int EPI = 0>
 __global__ __launch_bounds__(64 * NW * KS)
 void mx_gemm_decode(GemmArgs p)
 {
     using D = DecodeGeom<F, MT, NW, KMAX, KS>;
     constexpr int NWT = D::NWT;
+    static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
     constexpr int LB = 4;
     constexpr int PSA = D::PSA, PSB = D::PSB;
     static_assert(G * LB + D::PA + PSA + PSB < 64, "outstanding loads must fit the vmcnt field");
@@ -280,6 +284,31 @@ void mx_gemm_decode(GemmArgs p)
             if (i0 + decltype(uc)::value < nt)
                 stage(uc, i0 + decltype(uc)::value);
         });
+
+    if constexpr (EPI) {
+        // every K part parks its partial tile in the A region (free once all
+        // waves are past the K loop); the parts are summed in part order
+        // while the epilogue writes the output, any thread taking any group
+        // of four columns (the MX kinds want a row's 32-column block in 8
+        // consecutive lanes)
+        constexpr int RS = D::BN + 4;   // padded row stride (floats)
+        static_assert(KS * D::BM * RS * 4 <= D::SA_OFF, "partial tiles must fit the A region");
+        float *red = reinterpret_cast<float *>(smem);
+        __syncthreads();   // every wave is done reading the A tile
+#pragma unroll
+        for (int x = 0; x < MT; ++x)
+            *reinterpret_cast<v4f *>(&red[(kh * D::BM + 16 * x + r) * RS + 16 * rw + 4 * g]) = acc[x];
+        __syncthreads();
+        store_reduced_tile<OUT, 1, D::BM, D::BN / 4>(
+            p, m0, n0, (int)threadIdx.x, 64 * NWT, [&](int row, int c4) {
+                v4f sum = *reinterpret_cast<const v4f *>(&red[row * RS + 4 * c4]);
+#pragma unroll
+                for (int q = 1; q < KS; ++q)
+                    sum += *reinterpret_cast<const v4f *>(&red[(q * D::BM + row) * RS + 4 * c4]);
+                return sum;
+            });
+        return;
+    }
 
     if constexpr (KS > 1) {
         // the K parts past the first park their partial tiles in the A

@@ -131,4 +131,63 @@ __device__ __forceinline__ unsigned amax_pairs(const unsigned (&w)[NP])
     return m;
 }
 
+// Output of a workgroup tile reduced in LDS (the decode-width kernels).
+// Thread tid of nthr takes the groups of four consecutive columns q = tid,
+// tid + nthr, ... of a ROWS x 4*CG tile, in row-major group order (row =
+// q / CG, column group c4 = q % CG), whose FP32 values quad(row, c4)
+// returns; with EPI it applies bias and activation, then writes output kind
+// OUT at C[m0 + row][n0 + 4*c4 ..]:
+//   * BF16 / FP16 / FP32: one bounds-checked store per group;
+//   * MX kinds: the eight consecutive groups of a row's 32-column block
+//     share its amax over three lane exchanges.  N % 32 == 0 and CG % 8 == 0,
+//     so a block lies wholly inside or outside C; nthr and ROWS * CG are
+//     multiples of 64, so whole waves take part in the exchanges.
+template <int OUT, int EPI, int ROWS, int CG, class Quad>
+__device__ __forceinline__ void store_reduced_tile(const GemmArgs &p, int m0, int n0, int tid, int nthr,
+                                                   Quad &&quad)
+{
+    constexpr int NQ = ROWS * CG;
+    if constexpr (OUT == OUT_MX8 || OUT == OUT_MX4) {
+        static_assert(CG % 8 == 0 && NQ % 64 == 0, "MX output needs whole 32-column blocks and whole waves");
+        constexpr int QF = OUT == OUT_MX4 ? FMT_FP4 : FMT_FP8;
+        const int wave0 = tid & ~63;
+        for (int q0 = 0; q0 < NQ; q0 += nthr) {
+            if (q0 + wave0 >= NQ)          // NQ is a multiple of 64: wave-uniform
+                break;
+            const int q = q0 + tid;
+            const int row = q / CG, c4 = q % CG;
+            const int m = m0 + row, n = n0 + 4 * c4;
+            const v4f sum = epilogue4(quad(row, c4), p, n);
+            const unsigned w2[2] = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+            unsigned amax = amax_pairs(w2);
+            amax = max(amax, (unsigned)__shfl_xor((int)amax, 1, 64));
+            amax = max(amax, (unsigned)__shfl_xor((int)amax, 2, 64));
+            amax = max(amax, (unsigned)__shfl_xor((int)amax, 4, 64));
+            const unsigned sc = block_scale_code<QF>(amax);
+            unsigned code[1];
+            mx_codes<QF, 2>(w2, sc, code);
+            if (m < p.M && n < p.N) {
+                uint8_t *c8 = static_cast<uint8_t *>(p.c);
+                if constexpr (QF == FMT_FP4)
+                    *reinterpret_cast<uint16_t *>(c8 + (size_t)m * (p.N / 2) + n / 2) = (uint16_t)code[0];
+                else
+                    *reinterpret_cast<unsigned *>(c8 + (size_t)m * p.N + n) = code[0];
+                if ((c4 & 7) == 0)
+                    p.c_scale[(size_t)m * (p.N / 32) + n / 32] = (uint8_t)sc;
+            }
+        }
+    } else {
+        const bool vec_ok = (p.N & 3) == 0;
+        for (int q = tid; q < NQ; q += nthr) {
+            const int row = q / CG, c4 = q % CG;
+            const int m = m0 + row, n = n0 + 4 * c4;
+            v4f sum = quad(row, c4);
+            if constexpr (EPI)
+                sum = epilogue4(sum, p, n);
+            if (m < p.M && n < p.N)
+                store4<OUT>(p.c, p.N, m, n, sum, vec_ok && n + 3 < p.N);
+        }
+    }
+}
+
 }  // namespace mxg

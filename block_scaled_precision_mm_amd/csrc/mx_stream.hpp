@@ -274,55 +274,15 @@ void mx_gemm_stream(GemmArgs p)
             for (int y = 0; y < WN; ++y)
                 *reinterpret_cast<v4f *>(&red[kw][16 * x + r][16 * y + 4 * g]) = acc[x][y];
         __syncthreads();
-        constexpr int NQ = 16 * MT * 4 * WN;   // float4 column groups in the tile
-        if constexpr (OUT == OUT_MX8 || OUT == OUT_MX4) {
-            // MX output: the 8 consecutive lanes of one row's 32-column block
-            // share its amax; N % 32 == 0, so a block is wholly inside or out
-            static_assert(WN % 2 == 0, "MX output needs whole 32-column blocks per workgroup");
-            constexpr int QF = OUT == OUT_MX4 ? FMT_FP4 : FMT_FP8;
-            for (int q0 = 0; q0 < NQ; q0 += 64 * KW) {
-                if (q0 + 64 * kw >= NQ)        // NQ is a multiple of 64: wave-uniform
-                    break;
-                const int q = q0 + (int)threadIdx.x;
-                const int row = q / (4 * WN), c4 = q % (4 * WN);
+        // the KW partials summed in wave order while the output is written
+        store_reduced_tile<OUT, EPI, 16 * MT, 4 * WN>(
+            p, m0, n0, (int)threadIdx.x, 64 * KW, [&](int row, int c4) {
                 v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
 #pragma unroll
                 for (int w = 1; w < KW; ++w)
                     sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
-                const int m = m0 + row, n = n0 + 4 * c4;
-                sum = epilogue4(sum, p, n);
-                const unsigned w2[2] = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
-                unsigned amax = amax_pairs(w2);
-                amax = max(amax, (unsigned)__shfl_xor((int)amax, 1, 64));
-                amax = max(amax, (unsigned)__shfl_xor((int)amax, 2, 64));
-                amax = max(amax, (unsigned)__shfl_xor((int)amax, 4, 64));
-                const unsigned sc = block_scale_code<QF>(amax);
-                unsigned code[1];
-                mx_codes<QF, 2>(w2, sc, code);
-                if (m < p.M && n < p.N) {
-                    uint8_t *c8 = static_cast<uint8_t *>(p.c);
-                    if constexpr (QF == FMT_FP4)
-                        *reinterpret_cast<uint16_t *>(c8 + (size_t)m * (p.N / 2) + n / 2) = (uint16_t)code[0];
-                    else
-                        *reinterpret_cast<unsigned *>(c8 + (size_t)m * p.N + n) = code[0];
-                    if ((c4 & 7) == 0)
-                        p.c_scale[(size_t)m * (p.N / 32) + n / 32] = (uint8_t)sc;
-                }
-            }
-        } else {
-            for (int q = threadIdx.x; q < NQ; q += 64 * KW) {
-                const int row = q / (4 * WN), c4 = q % (4 * WN);
-                v4f sum = *reinterpret_cast<const v4f *>(&red[0][row][4 * c4]);
-#pragma unroll
-                for (int w = 1; w < KW; ++w)
-                    sum += *reinterpret_cast<const v4f *>(&red[w][row][4 * c4]);
-                const int m = m0 + row, n = n0 + 4 * c4;
-                if constexpr (EPI)
-                    sum = epilogue4(sum, p, n);
-                if (m < p.M && n < p.N)
-                    store4<OUT>(p.c, p.N, m, n, sum, vec_ok && n + 3 < p.N);
-            }
-        }
+                return sum;
+            });
     }
 }
 

@@ -161,6 +161,7 @@ struct FusedVariant {
     int threads;
     KernelFn fn[2][5];       // [fmt][out kind]
     int linear;
+    int kmax[2];             // largest K per format (0: any K)
 };
 #define MXG_FSFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O, 0, 1>)
 #define MXG_FSOUTS(F, MT, WN, KW)                                                                  \
@@ -168,13 +169,21 @@ struct FusedVariant {
      MXG_FSFN(F, MT, WN, KW, OUT_F32), MXG_FSFN(F, MT, WN, KW, OUT_MX8), MXG_FSFN(F, MT, WN, KW, OUT_MX4)}
 #define MXG_FSTREAM(MT, WN, KW)                                                                    \
     {"fstream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                                   \
-     {MXG_FSOUTS(FMT_FP8, MT, WN, KW), MXG_FSOUTS(FMT_FP4, MT, WN, KW)}, 0}
+     {MXG_FSOUTS(FMT_FP8, MT, WN, KW), MXG_FSOUTS(FMT_FP4, MT, WN, KW)}, 0, {0, 0}}
+#define MXG_FDFN(F, MT, NW, KM, G, KS, O) (&mx_gemm_decode<F, MT, NW, KM, G, O, KS, 1>)
+#define MXG_FDOUTS(F, MT, NW, KM, G, KS)                                                           \
+    {MXG_FDFN(F, MT, NW, KM, G, KS, OUT_BF16), MXG_FDFN(F, MT, NW, KM, G, KS, OUT_F16),            \
+     MXG_FDFN(F, MT, NW, KM, G, KS, OUT_F32), MXG_FDFN(F, MT, NW, KM, G, KS, OUT_MX8),             \
+     MXG_FDFN(F, MT, NW, KM, G, KS, OUT_MX4)}
+#define MXG_FDECODE(NAME, MT, NW, G, KS, K4, K8)                                                   \
+    {NAME, 16 * (MT), 16 * (NW), 64 * (NW) * (KS),                                                 \
+     {MXG_FDOUTS(FMT_FP8, MT, NW, K8, G, KS), MXG_FDOUTS(FMT_FP4, MT, NW, K4, G, KS)}, 0, {K8, K4}}
 #define MXG_FTFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O, 0, 1>)
 #define MXG_FTOUTS(F, MT, NT)                                                                      \
     {MXG_FTFN(F, MT, NT, OUT_BF16), MXG_FTFN(F, MT, NT, OUT_F16), MXG_FTFN(F, MT, NT, OUT_F32),    \
      MXG_FTFN(F, MT, NT, OUT_MX8), MXG_FTFN(F, MT, NT, OUT_MX4)}
 #define MXG_FTILE(NAME, MT, NT) \
-    {NAME, 64 * (MT), 64 * (NT), 256, {MXG_FTOUTS(FMT_FP8, MT, NT), MXG_FTOUTS(FMT_FP4, MT, NT)}, 1}
+    {NAME, 64 * (MT), 64 * (NT), 256, {MXG_FTOUTS(FMT_FP8, MT, NT), MXG_FTOUTS(FMT_FP4, MT, NT)}, 1, {0, 0}}
 
 const FusedVariant kFusedVariants[] = {
     MXG_FSTREAM(1, 2, 4),
@@ -182,6 +191,8 @@ const FusedVariant kFusedVariants[] = {
     MXG_FTILE("ftile_128x128", 2, 2),
     MXG_FTILE("ftile_256x128", 4, 2),
     MXG_FTILE("ftile_256x256", 4, 4),
+    MXG_FDECODE("fdecode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
+    MXG_FDECODE("fdecode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
 };
 constexpr int kNumFusedVariants = (int)(sizeof(kFusedVariants) / sizeof(kFusedVariants[0]));
 
@@ -437,8 +448,11 @@ int run_grouped(int is_fp4, const void *a, const void *b, const void *sa, const 
 // ------------------------------------------------------------ fused epilogue
 // Default fused kernel: the plain product's choice, among the kernels whose
 // workgroup tiles cover whole 32-column blocks.
-int pick_fused_variant(int64_t M, int64_t N)
+int pick_fused_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
+    // the plain product's decode-width choice (see pick_variant)
+    if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= 4096)
+        return M <= 16 ? 5 : 6;   // fdecode_16x64_k2 / fdecode_32x64_k2
     if (M <= 16)
         return 0;          // fstream_1x2_k4
     if (M <= 64)
@@ -474,10 +488,12 @@ int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const vo
             return MXG_ERR_SHAPE;
     }
     if (variant == kPickDefault)
-        variant = pick_fused_variant(M, N);
+        variant = pick_fused_variant(is_fp4, M, N, K);
     if (variant < 0 || variant >= kNumFusedVariants)
         return MXG_ERR_CONFIG;
     const FusedVariant &v = kFusedVariants[variant];
+    if (v.kmax[is_fp4 ? 1 : 0] && K > v.kmax[is_fp4 ? 1 : 0])
+        return MXG_ERR_CONFIG;
     const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
     if (v.linear ? gx * gy > INT32_MAX : (gx > INT32_MAX || gy > 65535))
         return MXG_ERR_SHAPE;
@@ -736,11 +752,19 @@ int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_s
 
 int mx_fused_num_variants(void) { return kNumFusedVariants; }
 
-int mx_fused_default_variant(int64_t M, int64_t N)
+int mx_fused_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
-    if (M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX)
+    if (M < 1 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX)
         return MXG_ERR_SHAPE;
-    return pick_fused_variant(M, N);
+    return pick_fused_variant(is_fp4 ? 1 : 0, M, N, K);
+}
+
+int64_t mx_fused_variant_max_k(int variant, int is_fp4)
+{
+    if (variant < 0 || variant >= kNumFusedVariants)
+        return MXG_ERR_CONFIG;
+    const int km = kFusedVariants[variant].kmax[is_fp4 ? 1 : 0];
+    return km ? km : kMaxK;
 }
 
 const char *mx_fused_variant_name(int variant)

@@ -233,8 +233,13 @@ int mx_scaled_mm_fused(int is_fp4, const void *a, const void *b, const void *a_s
                        mxg_stream_t stream);
 int mx_fused_num_variants(void);
 const char *mx_fused_variant_name(int variant);
-/* The variant mx_scaled_mm_fused picks for variant < 0, or MXG_ERR_SHAPE. */
-int mx_fused_default_variant(int64_t M, int64_t N);
+/* The variant mx_scaled_mm_fused picks for variant < 0 (is_fp4: 1 MXFP4,
+ * 0 MXFP8), or MXG_ERR_SHAPE for M, N or K < 1. */
+int mx_fused_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
+/* Largest K a fused variant accepts for the format (the decode-width
+ * variants keep the A tile in LDS); MXG_ERR_CONFIG for an unknown variant.
+ * A call with a larger K returns MXG_ERR_CONFIG. */
+int64_t mx_fused_variant_max_k(int variant, int is_fp4);
 
 /*
  * Dense BF16 / FP16 GEMM ("PyTorch 接上 FlyDSL", 5ulink.com, support-matrix
@@ -271,7 +276,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 6
+#define MXGEMM_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 6
+    assert lib.mx_abi_version() == 7
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -180,10 +180,25 @@ def test_fused_invalid_arguments(lib, args, status):
     assert rc == status, (rc, lib.mx_status_string(rc))
     n = lib.mx_fused_num_variants()
     assert n >= 1 and lib.mx_fused_variant_name(n) is None and lib.mx_fused_variant_name(0)
-    lib.mx_fused_default_variant.argtypes = [ctypes.c_int64, ctypes.c_int64]
-    for shape in ((1, 4096), (32, 14336), (64, 64), (256, 28672), (8192, 8192)):
-        assert 0 <= lib.mx_fused_default_variant(*shape) < n
-    assert lib.mx_fused_default_variant(0, 8) == -2
+    lib.mx_fused_default_variant.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.mx_fused_variant_max_k.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mx_fused_variant_max_k.restype = ctypes.c_int64
+    for is_fp4 in (0, 1):
+        for shape in ((1, 4096, 4096), (32, 14336, 4096), (32, 14336, 8192), (64, 64, 128),
+                      (256, 28672, 8192), (8192, 8192, 8192)):
+            v = lib.mx_fused_default_variant(is_fp4, *shape)
+            assert 0 <= v < n
+            # the default always accepts the K it was picked for
+            assert shape[2] <= lib.mx_fused_variant_max_k(v, is_fp4)
+    assert lib.mx_fused_default_variant(1, 0, 8, 128) == -2
+    assert lib.mx_fused_default_variant(1, 8, 8, 0) == -2
+    assert lib.mx_fused_variant_max_k(n, 1) == -9
+    # a fused variant with a K limit rejects a larger K before touching memory
+    for v in range(n):
+        km = lib.mx_fused_variant_max_k(v, 1)
+        if km < (1 << 22):
+            rc = lib.mx_scaled_mm_fused(1, A, A, A, A, 0, 0, A, A, 32, 64, km + 128, 0, v, None)
+            assert rc == -9, (v, rc)
 
 
 @pytest.mark.parametrize("args,status", [

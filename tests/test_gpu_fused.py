@@ -108,6 +108,7 @@ def test_every_variant_small(mx, fmt, act):
     # ragged M against every tile; N a multiple of 32 (MX output) but not of
     # the wider tiles; K several stages
     for v in range(mx.mx_fused_num_variants()):
+        assert 512 <= mx.mx_fused_variant_max_k(v, fmt == "fp4")
         check_case(mx, fmt, 70, 96, 512, act, True, v, seed=11 + act)
     check_case(mx, fmt, 5, 160, 256, act, False, 0, seed=21 + act)
 
@@ -123,3 +124,6 @@ def test_ragged_n_default(mx, fmt):
 def test_larger_default(mx, fmt):
     check_case(mx, fmt, 512, 1024, 1024, 3, True, -1, seed=41)
     check_case(mx, fmt, 32, 2048, 2048, 2, True, -1, seed=42)
+    # decode widths on wide N: the whole-row decode variants for E2M1
+    check_case(mx, fmt, 24, 8192, 1024, 1, True, -1, seed=43)
+    check_case(mx, fmt, 9, 8192, 640, 3, False, -1, seed=44)
