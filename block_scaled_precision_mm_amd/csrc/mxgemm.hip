@@ -288,6 +288,10 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant(N >= 8192 ? "skinny_64x64_k4" : "stream_2x2_k4");
     if (cdiv(M, 256) * cdiv(N, 256) >= 384)
         return find_variant("tile_256x256");
+    // from 256 rows the 128 x 256 tile (256 x 28672 x 8192: 57 us E2M1 and
+    // 93 us E4M3, against 61 and 96 for 256 x 128)
+    if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)
+        return find_variant("tile_128x256");
     if (cdiv(M, 256) * cdiv(N, 128) >= 192)
         return find_variant("tile_256x128");
     return find_variant("tile_128x128");
