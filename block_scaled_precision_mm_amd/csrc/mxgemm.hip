@@ -286,6 +286,15 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
     if (M <= 64)
         return find_variant(N >= 8192 ? "skinny_64x64_k4" : "stream_2x2_k4");
+    // 65-128 rows on narrow N give the tile kernels too few output tiles
+    // (128 x 4096 x 4096 E2M1: 17.3 us on tile_128x128, 7.9 on the decode
+    // kernel; 128 x 4096 x 14336: 56.8 against 21.5 on stream_4x2_k8)
+    if (M <= 128 && cdiv(M, 128) * cdiv(N, 128) < 64)
+        return find_variant(is_fp4 && K <= 4096 ? "decode_32x64_k2" : "stream_4x2_k8");
+    // and 129-256 rows (256 x 4096 x 4096: 12.0 us on stream_4x4_k4 against
+    // 17.3 on tile_128x128 for E2M1, 12.2 against 29.7 for E4M3)
+    if (M <= 256 && cdiv(M, 128) * cdiv(N, 128) <= 64)
+        return find_variant("stream_4x4_k4");
     if (cdiv(M, 256) * cdiv(N, 256) >= 384)
         return find_variant("tile_256x256");
     // from 256 rows the 128 x 256 tile (256 x 28672 x 8192: 57 us E2M1 and
