@@ -255,3 +255,37 @@ def test_default_variant(lib):
             assert 0 <= v < n, (shape, v)
     assert lib.mx_default_variant(1, 8, 8, 100) == -3
     assert lib.mx_default_variant(1, 0, 8, 128) == -2
+
+
+# The default choice shape by shape, as decided by the measured sweeps on
+# MI355X (the host half of the path: validate, pick, launch).
+DEFAULTS = [
+    # (is_fp4, M, N, K, variant)
+    (1, 32, 14336, 4096, "decode_32x64_k2"),
+    (1, 16, 14336, 4096, "decode_16x64_k2"),
+    (1, 8, 14336, 4096, "decode_16x64_k2"),
+    (1, 1, 14336, 4096, "stream_1x1_k4"),
+    (1, 32, 14336, 8192, "stream_2x4_k8"),     # K past the decode kernel's LDS-resident A tile
+    (0, 32, 14336, 4096, "stream_2x4_k8"),     # E4M3 decode widths stay on the stream kernel
+    (0, 8, 14336, 4096, "stream_1x2_k4"),
+    (1, 32, 4096, 4096, "stream_2x1_k4"),
+    (0, 64, 4096, 4096, "stream_2x2_k4"),
+    (1, 64, 14336, 4096, "skinny_64x64_k4"),
+    (1, 128, 4096, 4096, "decode_32x64_k2"),   # narrow N: too few tiles for the tile kernels
+    (1, 128, 4096, 14336, "stream_4x2_k8"),
+    (0, 128, 4096, 4096, "stream_4x2_k8"),
+    (1, 256, 4096, 4096, "stream_4x4_k4"),
+    (1, 128, 14336, 4096, "tile_128x128"),
+    (1, 256, 28672, 8192, "tile_128x256"),
+    (0, 256, 28672, 8192, "tile_128x256"),
+    (1, 8192, 8192, 8192, "tile_256x256"),
+]
+
+
+@pytest.mark.parametrize("is4,M,N,K,name", DEFAULTS, ids=lambda x: str(x))
+def test_default_variant_choice(lib, is4, M, N, K, name):
+    lib.mx_variant_max_k.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mx_variant_max_k.restype = ctypes.c_int64
+    v = lib.mx_default_variant(is4, M, N, K)
+    assert lib.mx_variant_name(v).decode() == name
+    assert K <= lib.mx_variant_max_k(v, is4)
