@@ -24,8 +24,10 @@
 //   * a K-contiguous operand: four lanes per row read its 64 bytes (16-byte
 //     loads) and store them as they are;
 //   * an M- or N-contiguous operand: sixteen lanes per K row read its 256
-//     bytes and each lane stores its 8 values as 8 two-byte writes into
-//     the K-contiguous rows (the transposition).
+//     bytes; a 4 x 4 transpose of dwords across the four K rows a wave holds
+//     (lane swaps between its 16-lane rows) leaves each lane two columns at
+//     four consecutive K values, stored as two 8-byte writes into the
+//     K-contiguous rows (the transposition).
 // Loads go through buffer resources over the whole operand: rows past M /
 // N and steps past K read as zeros, so tails need no branches.  Operand
 // rows must be 16-byte aligned (the contiguous dimension a multiple of 8)
@@ -106,10 +108,32 @@ struct DenseLoader {
             if constexpr (KC) {
                 *reinterpret_cast<u4v *>(s + (t / 4 + 64 * j) * DenseTile::LDK + 8 * (t % 4)) = v[j];
             } else {
-                const int k = t / 16 + 16 * j, c0 = 8 * (t % 16);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    s[(c0 + i) * DenseTile::LDK + k] = (uint16_t)(v[j][i / 2] >> (16 * (i % 2)));
+                // The four 16-lane rows of a wave hold four consecutive K
+                // rows (t / 16) of the same 128 columns, lane p of a row
+                // columns 8p .. 8p+7, dword d = columns 8p+2d, 8p+2d+1.  A
+                // 4 x 4 dword transpose across the rows (two permlane32 and
+                // two permlane16 swaps, gfx950) leaves row q with dword q of
+                // all four K rows, i.e. columns 8p+2q and 8p+2q+1 at four
+                // consecutive K: two 8-byte stores instead of eight 2-byte
+                // ones (which all fell on the same two LDS banks).
+                const int q = (t >> 4) & 3, p = t & 15, w = t >> 6;
+                unsigned x0 = v[j][0], x1 = v[j][1], x2 = v[j][2], x3 = v[j][3];
+                const auto a = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+                const auto b = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+                const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+                const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+                x0 = c[0];   // x_i: columns 8p+2q, 8p+2q+1 at K row 4w + 16j + i
+                x1 = c[1];
+                x2 = d[0];
+                x3 = d[1];
+                const int col = 8 * p + 2 * q, k = 16 * j + 4 * w;
+                u2v lo, hi;
+                lo.x = (x0 & 0xFFFFu) | (x1 << 16);
+                lo.y = (x2 & 0xFFFFu) | (x3 << 16);
+                hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
+                hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
+                *reinterpret_cast<u2v *>(s + col * DenseTile::LDK + k) = lo;
+                *reinterpret_cast<u2v *>(s + (col + 1) * DenseTile::LDK + k) = hi;
             }
         }
     }
