@@ -132,8 +132,13 @@ struct DenseLoader {
                 lo.y = (x2 & 0xFFFFu) | (x3 << 16);
                 hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
                 hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
-                *reinterpret_cast<u2v *>(s + col * DenseTile::LDK + k) = lo;
-                *reinterpret_cast<u2v *>(s + (col + 1) * DenseTile::LDK + k) = hi;
+                // odd column groups store their odd column first, so that one
+                // store instruction covers all eight column residues mod 8
+                // (the 80-byte row stride maps a column to its LDS bank
+                // group by that residue)
+                const bool odd = p & 1;
+                *reinterpret_cast<u2v *>(s + (col + odd) * DenseTile::LDK + k) = odd ? hi : lo;
+                *reinterpret_cast<u2v *>(s + (col + !odd) * DenseTile::LDK + k) = odd ? lo : hi;
             }
         }
     }
