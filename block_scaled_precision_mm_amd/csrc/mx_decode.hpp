@@ -16,9 +16,9 @@
 //   * issue order: the A tile and the scale codes are requested first and
 //     are the only loads the workgroup waits for before its one barrier; the
 //     B ring is already in flight behind them, so HBM streams from the start.
-//     A ring of three 256-byte stages per wave (12 KB) beat deeper ones
-//     (four to eight stages) on MI355X, and non-temporal B loads (B is read
-//     once) gained about 1 us at 32 x 14336 x 4096.
+//     With one wave per row group, a ring of three 256-byte stages (12 KB)
+//     beat deeper ones (four to eight stages) on MI355X; non-temporal B
+//     loads (B is read once) gained about 1 us at 32 x 14336 x 4096.
 // So:
 //   * a workgroup owns 16*NW consecutive B rows and all 16*MT A rows; each
 //     16-row group of B is streamed by KS waves, wave (w, q) taking rows
@@ -31,8 +31,11 @@
 //     once into LDS (hence the K limit KMAX: the A tile must fit);
 //   * B stages of 256 bytes per row are loaded with 16-byte loads in which
 //     16 consecutive lanes read one row's 256 contiguous bytes, into a
-//     G-deep register ring, stored into one of two private LDS slots and
-//     read back as 16x16x128 MFMA fragments.
+//     G-deep register ring, stored into the wave's private LDS slot (two
+//     alternating slots when KS = 1) and read back as 16x16x128 MFMA
+//     fragments;
+//   * with EPI the summed tile goes through LDS to the shared reduced-tile
+//     epilogue (bias, activation, 16-bit / FP32 or MX-requantized output).
 //
 // LDS layouts: code rows in groups of 8, chunk-major inside a group (chunk c
 // of the 8 rows = 128 contiguous bytes) with a padded chunk stride of 160
