@@ -193,6 +193,7 @@ const FusedVariant kFusedVariants[] = {
     MXG_FTILE("ftile_256x256", 4, 4),
     MXG_FDECODE("fdecode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
     MXG_FDECODE("fdecode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
+    MXG_FTILE("ftile_128x256", 2, 4),
 };
 constexpr int kNumFusedVariants = (int)(sizeof(kFusedVariants) / sizeof(kFusedVariants[0]));
 
@@ -472,6 +473,8 @@ int pick_fused_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return 1;          // fstream_2x4_k8
     if (cdiv(M, 256) * cdiv(N, 256) >= 384)
         return 4;          // ftile_256x256
+    if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)
+        return 7;          // ftile_128x256 (the plain product's rule)
     if (cdiv(M, 256) * cdiv(N, 128) >= 192)
         return 3;          // ftile_256x128
     return 2;              // ftile_128x128
