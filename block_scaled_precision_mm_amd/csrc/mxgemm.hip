@@ -381,18 +381,27 @@ int validate_grouped(const void *a, const void *b, const void *sa, const void *s
 // Default grouped kernel from the mean rows per group (MI355X sweeps: up to
 // 16 rows a group the product is a B stream -- 256 rows over 32 experts at
 // N = K = 2048 MXFP8 ran 31.9 us on gstream_1x2_k4, 40.8 on gstream_2x4_k8).
+int find_group_variant(const char *name)
+{
+    for (int i = 0; i < kNumGroupVariants; ++i)
+        if (strcmp(kGroupVariants[i].name, name) == 0)
+            return i;
+    return 0;
+}
+
 int pick_group_variant(int64_t groups, int64_t M, int64_t N)
 {
     (void)N;
     const int64_t mean = M / groups;
     if (mean <= 16)
-        return 0;          // gstream_1x2_k4
+        return find_group_variant("gstream_1x2_k4");
     if (mean <= 48)
-        return 1;          // gstream_2x4_k8
+        return find_group_variant("gstream_2x4_k8");
     if (mean <= 192)
-        return 2;          // gtile_128x128
-    return 4;              // gtile_256x256 (8 x 1024 rows, N = K = 4096, MXFP8:
-                           // 190 us against 226 for 256x128 and 242 for 128x128)
+        return find_group_variant("gtile_128x128");
+    // 8 x 1024 rows, N = K = 4096, MXFP8: 190 us against 226 for 256x128 and
+    // 242 for 128x128
+    return find_group_variant("gtile_256x256");
 }
 
 int launch_grouped(int is_fp4, const void *a, const void *b, const void *sa, const void *sb,
@@ -462,22 +471,30 @@ int run_grouped(int is_fp4, const void *a, const void *b, const void *sa, const 
 // ------------------------------------------------------------ fused epilogue
 // Default fused kernel: the plain product's choice, among the kernels whose
 // workgroup tiles cover whole 32-column blocks.
+int find_fused_variant(const char *name)
+{
+    for (int i = 0; i < kNumFusedVariants; ++i)
+        if (strcmp(kFusedVariants[i].name, name) == 0)
+            return i;
+    return 0;
+}
+
 int pick_fused_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     // the plain product's decode-width choice (see pick_variant)
     if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= 4096)
-        return M <= 16 ? 5 : 6;   // fdecode_16x64_k2 / fdecode_32x64_k2
+        return find_fused_variant(M <= 16 ? "fdecode_16x64_k2" : "fdecode_32x64_k2");
     if (M <= 16)
-        return 0;          // fstream_1x2_k4
+        return find_fused_variant("fstream_1x2_k4");
     if (M <= 64)
-        return 1;          // fstream_2x4_k8
+        return find_fused_variant("fstream_2x4_k8");
     if (cdiv(M, 256) * cdiv(N, 256) >= 384)
-        return 4;          // ftile_256x256
-    if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)
-        return 7;          // ftile_128x256 (the plain product's rule)
+        return find_fused_variant("ftile_256x256");
+    if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)   // the plain product's rule
+        return find_fused_variant("ftile_128x256");
     if (cdiv(M, 256) * cdiv(N, 128) >= 192)
-        return 3;          // ftile_256x128
-    return 2;              // ftile_128x128
+        return find_fused_variant("ftile_256x128");
+    return find_fused_variant("ftile_128x128");
 }
 
 int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const void *sb,
