@@ -118,6 +118,9 @@ const Variant kVariants[] = {
     MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048),
     MXG_DECODE("decode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
     MXG_DECODE("decode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
+    // the same with room for a longer A tile (more LDS: 1-2% slower at K <= 4096)
+    MXG_DECODE("decode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048),
+    MXG_DECODE("decode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048),
 
     MXG_SKINNY("skinny_32x64_k4",   1, 2, 4, 4),
     MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
@@ -194,6 +197,8 @@ const FusedVariant kFusedVariants[] = {
     MXG_FDECODE("fdecode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
     MXG_FDECODE("fdecode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
     MXG_FTILE("ftile_128x256", 2, 4),
+    MXG_FDECODE("fdecode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048),
+    MXG_FDECODE("fdecode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048),
 };
 constexpr int kNumFusedVariants = (int)(sizeof(kFusedVariants) / sizeof(kFusedVariants[0]));
 
@@ -275,12 +280,17 @@ int find_variant(const char *name)
 // columns, so bigger tiles move fewer bytes per FLOP).
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
-    // E2M1, 5-32 rows, wide N, A tile fits LDS: the whole-row decode kernel
-    // with two waves per row group (32 x 14336 x 4096: 9.2 us against 9.8
-    // with one wave and 10.6 for stream_2x4_k8; 16 rows: 8.4 against 9.4
-    // for stream_1x1_k4); at 1-4 rows the narrow stream tile is faster
-    if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= 4096)
-        return find_variant(M <= 16 ? "decode_16x64_k2" : "decode_32x64_k2");
+    // E2M1, 5-32 rows, wide N, A tile fits LDS (K up to 8192 for 16 rows,
+    // 5120 for 32): the whole-row decode kernel with two waves per row group
+    // (32 x 14336 x 4096: 9.2 us against 9.8 with one wave and 10.6 for
+    // stream_2x4_k8; 32 x 25600 x 5120: 18.8 against 23.5; 16 x 14336 x 8192:
+    // 13.4 against 19.7 for stream_1x1_k4); at 1-4 rows the narrow stream
+    // tile is faster
+    if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= (M <= 16 ? 8192 : 5120)) {
+        if (K <= 4096)
+            return find_variant(M <= 16 ? "decode_16x64_k2" : "decode_32x64_k2");
+        return find_variant(M <= 16 ? "decode_16x64_k2_long" : "decode_32x64_k2_long");
+    }
     if (M <= 16)
         return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
     if (M <= 32)
@@ -291,7 +301,8 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     // (128 x 4096 x 4096 E2M1: 17.3 us on tile_128x128, 7.9 on the decode
     // kernel; 128 x 4096 x 14336: 56.8 against 21.5 on stream_4x2_k8)
     if (M <= 128 && cdiv(M, 128) * cdiv(N, 128) < 64)
-        return find_variant(is_fp4 && K <= 4096 ? "decode_32x64_k2" : "stream_4x2_k8");
+        return find_variant(!is_fp4 || K > 5120 ? "stream_4x2_k8"
+                            : K <= 4096 ? "decode_32x64_k2" : "decode_32x64_k2_long");
     // and 129-256 rows (256 x 4096 x 4096: 12.0 us on stream_4x4_k4 against
     // 17.3 on tile_128x128 for E2M1, 12.2 against 29.7 for E4M3)
     if (M <= 256 && cdiv(M, 128) * cdiv(N, 128) <= 64)
@@ -482,8 +493,11 @@ int find_fused_variant(const char *name)
 int pick_fused_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     // the plain product's decode-width choice (see pick_variant)
-    if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= 4096)
-        return find_fused_variant(M <= 16 ? "fdecode_16x64_k2" : "fdecode_32x64_k2");
+    if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= (M <= 16 ? 8192 : 5120)) {
+        if (K <= 4096)
+            return find_fused_variant(M <= 16 ? "fdecode_16x64_k2" : "fdecode_32x64_k2");
+        return find_fused_variant(M <= 16 ? "fdecode_16x64_k2_long" : "fdecode_32x64_k2_long");
+    }
     if (M <= 16)
         return find_fused_variant("fstream_1x2_k4");
     if (M <= 64)

@@ -266,6 +266,9 @@ DEFAULTS = [
     (1, 8, 14336, 4096, "decode_16x64_k2"),
     (1, 1, 14336, 4096, "stream_1x1_k4"),
     (1, 32, 14336, 8192, "stream_2x4_k8"),     # K past the decode kernel's LDS-resident A tile
+    (1, 32, 25600, 5120, "decode_32x64_k2_long"),
+    (1, 16, 14336, 8192, "decode_16x64_k2_long"),
+    (1, 128, 4096, 5120, "decode_32x64_k2_long"),
     (0, 32, 14336, 4096, "stream_2x4_k8"),     # E4M3 decode widths stay on the stream kernel
     (0, 8, 14336, 4096, "stream_1x2_k4"),
     (1, 32, 4096, 4096, "stream_2x1_k4"),

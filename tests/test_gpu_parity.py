@@ -98,6 +98,21 @@ def test_small_shapes_every_variant(mx, fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_variants_at_their_largest_k(mx, fmt):
+    # the variants that keep the A tile in LDS, at the largest K they take
+    # (every A chunk and scale step slot in use), ragged M and N
+    M, N = 29, 200
+    for v in range(mx.mx_num_variants()):
+        K = mx.mx_variant_max_k(v, fmt == "fp4")
+        if K >= (1 << 22):
+            continue
+        a, b, sa, sb = quantized(fmt, M, N, K, seed=9000 + K + v)
+        print("largest K", fmt, mx.mx_variant_name(v), K, flush=True)
+        full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v,
+                   what="%s %s K=%d" % (fmt, mx.mx_variant_name(v), K))
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
 def test_default_path_random_codes_wide_scales(mx, fmt):
     # uniformly random codes (every element code, incl. subnormals) and scales over 2^+-14
     M, N, K = 70, 90, 1024
