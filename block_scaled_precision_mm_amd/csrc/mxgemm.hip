@@ -97,6 +97,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
+    MXG_STREAM(1, 1, 16),
     MXG_STREAM(1, 2, 4),
     MXG_STREAM(1, 4, 4),
     MXG_STREAM(2, 1, 4),
@@ -291,6 +292,10 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
             return find_variant(M <= 16 ? "decode_16x64_k2" : "decode_32x64_k2");
         return find_variant(M <= 16 ? "decode_16x64_k2_long" : "decode_32x64_k2_long");
     }
+    // long K splits over sixteen waves (8 x 4096 x 14336 E2M1: 8.4 us against
+    // 10.3 with four)
+    if (M <= 16 && is_fp4 && K >= 8192)
+        return find_variant("stream_1x1_k16");
     if (M <= 16)
         return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
     if (M <= 32)

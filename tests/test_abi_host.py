@@ -265,6 +265,8 @@ DEFAULTS = [
     (1, 16, 14336, 4096, "decode_16x64_k2"),
     (1, 8, 14336, 4096, "decode_16x64_k2"),
     (1, 1, 14336, 4096, "stream_1x1_k4"),
+    (1, 8, 4096, 14336, "stream_1x1_k16"),
+    (1, 1, 4096, 14336, "stream_1x1_k16"),
     (1, 32, 14336, 8192, "stream_2x4_k8"),     # K past the decode kernel's LDS-resident A tile
     (1, 32, 25600, 5120, "decode_32x64_k2_long"),
     (1, 16, 14336, 8192, "decode_16x64_k2_long"),
