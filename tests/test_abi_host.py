@@ -281,6 +281,7 @@ DEFAULTS = [
     (0, 128, 4096, 4096, "stream_4x2_k8"),
     (1, 256, 4096, 4096, "stream_4x4_k4"),
     (1, 128, 14336, 4096, "tile_128x128"),
+    (1, 128, 25600, 5120, "tile_128x128"),     # no half-empty 256-row tiles
     (1, 256, 28672, 8192, "tile_128x256"),
     (0, 256, 28672, 8192, "tile_128x256"),
     (1, 8192, 8192, 8192, "tile_256x256"),
