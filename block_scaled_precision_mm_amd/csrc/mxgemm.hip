@@ -313,8 +313,11 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     if (M <= 256 && cdiv(M, 128) * cdiv(N, 128) <= 64)
         return find_variant("stream_4x4_k4");
     // tiles of 256 rows only above 128 rows, where they are not half empty
-    // (128 x 25600 x 5120 E2M1: 29.1 us on 128 x 128, 32.7 on 256 x 128)
-    if (M > 128 && cdiv(M, 256) * cdiv(N, 256) >= 384)
+    // (128 x 25600 x 5120 E2M1: 29.1 us on 128 x 128, 32.7 on 256 x 128);
+    // 256 x 256 from 192 tiles (512 x 25600 x 5120: 55.5 us, against 71.8 on
+    // 128 x 256; at 112 tiles, 512 x 14336 x 4096, 128 x 256 wins: 31.0
+    // against 37.8)
+    if (M > 128 && cdiv(M, 256) * cdiv(N, 256) >= 192)
         return find_variant("tile_256x256");
     // from 256 rows the 128 x 256 tile (256 x 28672 x 8192: 57 us E2M1 and
     // 93 us E4M3, against 61 and 96 for 256 x 128)

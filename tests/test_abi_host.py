@@ -285,6 +285,8 @@ DEFAULTS = [
     (1, 256, 28672, 8192, "tile_128x256"),
     (0, 256, 28672, 8192, "tile_128x256"),
     (1, 8192, 8192, 8192, "tile_256x256"),
+    (1, 512, 25600, 5120, "tile_256x256"),
+    (1, 512, 14336, 4096, "tile_128x256"),
 ]
 
 
