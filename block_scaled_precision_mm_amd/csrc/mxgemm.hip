@@ -513,7 +513,7 @@ int pick_fused_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     if (M <= 64)
         return find_fused_variant("fstream_2x4_k8");
     // the plain product's tile rule
-    if (M > 128 && cdiv(M, 256) * cdiv(N, 256) >= 384)
+    if (M > 128 && cdiv(M, 256) * cdiv(N, 256) >= 192)
         return find_fused_variant("ftile_256x256");
     if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)
         return find_fused_variant("ftile_128x256");
