@@ -30,10 +30,16 @@
 //   * the A tile and the scale codes of all the workgroup's rows are loaded
 //     once into LDS (hence the K limit KMAX: the A tile must fit);
 //   * B stages of 256 bytes per row are loaded with 16-byte loads in which
-//     16 consecutive lanes read one row's 256 contiguous bytes, into a
-//     G-deep register ring, stored into the wave's private LDS slot (two
-//     alternating slots when KS = 1) and read back as 16x16x128 MFMA
-//     fragments;
+//     16 consecutive lanes read one row's 256 contiguous bytes (loading the
+//     fragments straight into registers instead, 64 bytes of 16 rows per
+//     load, streamed B slower), and reach the wave's LDS in one of two ways:
+//     a G-deep register ring stored stage by stage into the wave's private
+//     slot (two alternating slots when KS = 1), or (DMA) G slots that the
+//     buffer loads write themselves, each lane's chunk XOR-swizzled by its
+//     row -- no staging registers and no LDS store instructions (32 x 14336
+//     x 4096 with one wave per row group and three slots: 8.6 us against
+//     9.0-9.4 with two waves and register rings).  Either is read back as
+//     16x16x128 MFMA fragments;
 //   * with EPI the summed tile goes through LDS to the shared reduced-tile
 //     epilogue (bias, activation, 16-bit / FP32 or MX-requantized output).
 //
@@ -99,6 +105,11 @@ struct DecodeGeom {
     {
         return (row >> 3) * (SCH * CHUNK) + c * CHUNK + (row & 7) * 16;
     }
+    // LDS ring (the loads write LDS themselves): one unpadded 16-row stage
+    // per slot, chunk c of row r at 16 (c ^ r) -- the 16 rows of a fragment
+    // read then fall on 16 different 4-bank groups
+    static constexpr int DSLOT = 16 * SW;
+    __device__ static constexpr int d_off(int row, int c) { return 256 * row + 16 * (c ^ row); }
 };
 
 // Wait until at most `later` stages of LB loads each are outstanding.
@@ -117,7 +128,10 @@ __device__ __forceinline__ void wait_later(int later)
 
 // EPI: the fused epilogue (bias, activation, and the MX output kinds) on
 // the final tile, which then goes through LDS.
-template <int F, int MT, int NW, int KMAX, int G, int OUT, int KS = 1, int EPI = 0>
+// DMA: the B ring lives in LDS, G slots per wave that the buffer loads write
+// directly (no register staging and no LDS store instructions); otherwise
+// it is a register ring stored into the wave's LDS slot stage by stage.
+template <int F, int MT, int NW, int KMAX, int G, int OUT, int KS = 1, int EPI = 0, int DMA = 0>
 __global__ __launch_bounds__(64 * NW * KS)
 void mx_gemm_decode(GemmArgs p)
 {
@@ -127,7 +141,9 @@ void mx_gemm_decode(GemmArgs p)
     constexpr int LB = 4;
     constexpr int PSA = D::PSA, PSB = D::PSB;
     static_assert(G * LB + D::PA + PSA + PSB < 64, "outstanding loads must fit the vmcnt field");
-    __shared__ __attribute__((aligned(1024))) char smem[D::BYTES];
+    constexpr int LDS_BYTES = DMA ? D::B_OFF + NWT * G * D::DSLOT : D::BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -175,9 +191,12 @@ void mx_gemm_decode(GemmArgs p)
         svb[i] = load16<CPOL_NONE>(rsb, c < sb_chunks ? row * p.srow_bytes + 16u * (c - row * CQ) : kOutOfRange);
     }
 
+    // load j of a stage covers rows 4j .. 4j+3 of this wave's 16 (lane l:
+    // row 4j + l/16, 16 bytes of the stage's 256 at chunk l%16, XOR the row
+    // with the LDS ring), read once, so non-temporal
     const unsigned bload = (unsigned)(16 * rw + (lane >> 4)) * p.row_bytes + 16u * (unsigned)(lane & 15);
     const unsigned bstride = 4u * p.row_bytes;
-    u4v stg[G][LB];
+    u4v stg[DMA ? 1 : G][LB];
     // stages past K read zeros but are issued all the same, so that the
     // outstanding-load counts below are exact
     auto fill_stage = [&](u4v (&set)[LB], int i) {   // the wave's i-th stage
@@ -186,9 +205,25 @@ void mx_gemm_decode(GemmArgs p)
         for (int j = 0; j < LB; ++j)
             set[j] = load16<CPOL_NT>(rb, bload + (unsigned)j * bstride + kt);
     };
+    char *ring = smem + D::B_OFF + wave * G * D::DSLOT;   // DMA: this wave's G slots
+    auto fill_slot = [&](int u, int i) {   // the wave's i-th stage into LDS slot u
+        const unsigned kt = i < nt ? (unsigned)(t0 + i) * D::SW : kOutOfRange;
+        const unsigned brow = (unsigned)(16 * rw + (lane >> 4)) * p.row_bytes;
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-        fill_stage(stg[i], i);
+        for (int j = 0; j < LB; ++j) {
+            // lane l lands at byte 1024 j + 16 l of the slot = d_off(row, l%16 ^ row)
+            const unsigned c = (unsigned)(lane & 15) ^ (unsigned)(4 * j + (lane >> 4));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(ring + u * D::DSLOT + 1024 * j), 16,
+                                                     brow + (unsigned)j * bstride + 16u * c + kt, 0, 0, CPOL_NT);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        if constexpr (DMA)
+            fill_slot(i, i);
+        else
+            fill_stage(stg[i], i);
+    }
 
     wait_vm<G * LB>();   // the A tile and the scale pieces have landed
 #pragma unroll
@@ -223,9 +258,7 @@ void mx_gemm_decode(GemmArgs p)
     }
     __syncthreads();   // the A tile and scale codes are shared by all waves
 
-    // ---- B ring: load j of a stage covers rows 4j .. 4j+3 of this wave's 16
-    // (lane l: row 4j + l/16, bytes 16*(l%16) of the stage's 256), read once,
-    // so non-temporal
+    // register ring: each stage is stored into the wave's LDS slot(s)
     char *slots = smem + D::B_OFF + wave * D::SLOTS * D::SLOT;
     const int bw_lane = D::b_off(lane >> 4, lane & 15);
     auto store_stage = [&](const u4v (&set)[LB], int i) {
@@ -242,15 +275,19 @@ void mx_gemm_decode(GemmArgs p)
 
     // one stage (the wave's i-th): wait for its loads (the stages issued
     // after it may stay in flight: the prologue issued G, each earlier stage
-    // refilled one below nt), store it, refill its staging set, then its
-    // MFMA steps
+    // refilled one below nt); register ring: store it and refill its staging
+    // set, then its MFMA steps; LDS ring: its MFMA steps, then the refill of
+    // its slot
     auto stage = [&](auto uc, int i) {
         constexpr int u = decltype(uc)::value;
         wait_later<LB, G>(min(i + G, max(G, nt)) - i - 1);
-        store_stage(stg[u], i);
-        if (i + G < nt)
-            fill_stage(stg[u], i + G);
-        const char *slot = slots + (D::SLOTS == 2 ? (i & 1) * D::SLOT : 0);
+        if constexpr (!DMA) {
+            store_stage(stg[u], i);
+            if (i + G < nt)
+                fill_stage(stg[u], i + G);
+        }
+        const char *slot = DMA ? ring + u * D::DSLOT : slots + (D::SLOTS == 2 ? (i & 1) * D::SLOT : 0);
+        auto boff = [&](int c) { return DMA ? D::d_off(r, c) : D::b_off(r, c); };
         const int t = t0 + i;
 #pragma unroll
         for (int s = 0; s < D::SPS; ++s) {
@@ -259,10 +296,10 @@ void mx_gemm_decode(GemmArgs p)
                 break;
             StepFrag<F> fb, fa[MT];
             if constexpr (F == FMT_FP4) {
-                fb.d[0] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 4 * s + g));
+                fb.d[0] = *reinterpret_cast<const u4v *>(slot + boff(4 * s + g));
             } else {
-                fb.d[0] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + g));
-                fb.d[1] = *reinterpret_cast<const u4v *>(slot + D::b_off(r, 8 * s + 4 + g));
+                fb.d[0] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + g));
+                fb.d[1] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + 4 + g));
             }
             const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::BN + 16 * rw + r)) >> (8 * g);
             unsigned sa[MT];
@@ -281,12 +318,22 @@ void mx_gemm_decode(GemmArgs p)
             for (int x = 0; x < MT; ++x)
                 acc[x] = mfma<F>(fb, sb, fa[x], sa[x], acc[x]);
         }
+        if constexpr (DMA) {
+            if (i + G < nt) {
+                // the slot's fragment reads have returned before its next
+                // stage can land in it
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                fill_slot(u, i + G);
+            }
+        }
     };
     for (int i0 = 0; i0 < nt; i0 += G)
         static_for<G>([&](auto uc) {
             if (i0 + decltype(uc)::value < nt)
                 stage(uc, i0 + decltype(uc)::value);
         });
+    if constexpr (DMA)
+        wait_vm<0>();   // zero stages past nt may still be landing in the ring
 
     if constexpr (EPI) {
         // every K part parks its partial tile in the A region (free once all

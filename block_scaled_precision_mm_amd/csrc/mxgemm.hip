@@ -69,14 +69,16 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 
 // Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
 // (K up to K8 / K4 for FP8 / FP4), NW groups of 16 B rows, each streamed by
-// KS waves (one K part each) through private rings of G 256-byte stages.
-#define MXG_DFN(F, MT, NW, KM, G, O, KS) (&mx_gemm_decode<F, MT, NW, KM, G, O, KS>)
-#define MXG_DOUTS(F, MT, NW, KM, G, KS)                                                    \
-    {MXG_DFN(F, MT, NW, KM, G, OUT_BF16, KS), MXG_DFN(F, MT, NW, KM, G, OUT_F16, KS),        \
-     MXG_DFN(F, MT, NW, KM, G, OUT_F32, KS)}
-#define MXG_DECODE(NAME, MT, NW, G, KS, K4, K8)                                            \
-    {NAME, 16 * (MT), 16 * (NW), 64 * (NW) * (KS),                                         \
-     {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS)}, {K8, K4}, 0}
+// KS waves (one K part each) through private rings of G 256-byte stages,
+// held in LDS slots that the loads write directly (DMA = 1) or in registers.
+#define MXG_DFN(F, MT, NW, KM, G, O, KS, DMA) (&mx_gemm_decode<F, MT, NW, KM, G, O, KS, 0, DMA>)
+#define MXG_DOUTS(F, MT, NW, KM, G, KS, DMA)                                                     \
+    {MXG_DFN(F, MT, NW, KM, G, OUT_BF16, KS, DMA), MXG_DFN(F, MT, NW, KM, G, OUT_F16, KS, DMA),   \
+     MXG_DFN(F, MT, NW, KM, G, OUT_F32, KS, DMA)}
+#define MXG_DECODE(NAME, MT, NW, G, KS, K4, K8, DMA)                                           \
+    {NAME, 16 * (MT), 16 * (NW), 64 * (NW) * (KS),                                             \
+     {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS, DMA), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS, DMA)},   \
+     {K8, K4}, 0}
 
 // Decode-width tiles on the 32x32x64 instruction: waves split K, each
 // streams its run through a private register ring and LDS slot.
@@ -114,14 +116,14 @@ const Variant kVariants[] = {
     MXG_LDS("lds_32x64_w4",        1, 1, 4, 2, 1, 4, 2, 4, 4),
     MXG_LDS("lds_64x16_k4",        4, 1, 1, 4, 1, 2, 1, 3, 3),
     MXG_LDS("lds_32x32_k4",        4, 1, 1, 2, 2, 2, 1, 3, 3),
-    //          name              MT NW G  KS K4    K8
-    MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048),
-    MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048),
-    MXG_DECODE("decode_32x64_k2", 2, 4, 2, 2, 4096, 2048),
-    MXG_DECODE("decode_16x64_k2", 1, 4, 2, 2, 4096, 2048),
+    //          name              MT NW G  KS K4    K8    DMA
+    MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048, 1),
+    MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048, 1),
+    MXG_DECODE("decode_32x64_k2", 2, 4, 2, 2, 4096, 2048, 0),
+    MXG_DECODE("decode_16x64_k2", 1, 4, 2, 2, 4096, 2048, 0),
     // the same with room for a longer A tile (more LDS: 1-2% slower at K <= 4096)
-    MXG_DECODE("decode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048),
-    MXG_DECODE("decode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048),
+    MXG_DECODE("decode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048, 0),
+    MXG_DECODE("decode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048, 0),
 
     MXG_SKINNY("skinny_32x64_k4",   1, 2, 4, 4),
     MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
@@ -282,14 +284,17 @@ int find_variant(const char *name)
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     // E2M1, 5-32 rows, wide N, A tile fits LDS (K up to 8192 for 16 rows,
-    // 5120 for 32): the whole-row decode kernel with two waves per row group
-    // (32 x 14336 x 4096: 9.2 us against 9.8 with one wave and 10.6 for
-    // stream_2x4_k8; 32 x 25600 x 5120: 18.8 against 23.5; 16 x 14336 x 8192:
-    // 13.4 against 19.7 for stream_1x1_k4); at 1-4 rows the narrow stream
-    // tile is faster
+    // 5120 for 32): the whole-row decode kernel, at K <= 4096 with one wave
+    // per row group and its B ring in LDS (32 x 14336 x 4096: 8.6 us against
+    // 9.0-9.4 with two waves and register rings, 10.6 for stream_2x4_k8;
+    // 8 x 14336 x 4096: 7.7 against 7.9-8.3), above with two waves and
+    // register rings, whose smaller LDS footprint leaves room for the A tile
+    // (32 x 25600 x 5120: 18.8 against 23.5 for stream_2x4_k8; 16 x 14336 x
+    // 8192: 13.4 against 19.7 for stream_1x1_k4); at 1-4 rows the narrow
+    // stream tile is faster
     if (is_fp4 && M > 4 && M <= 32 && N >= 8192 && K <= (M <= 16 ? 8192 : 5120)) {
         if (K <= 4096)
-            return find_variant(M <= 16 ? "decode_16x64_k2" : "decode_32x64_k2");
+            return find_variant(M <= 16 ? "decode_16x64" : "decode_32x64");
         return find_variant(M <= 16 ? "decode_16x64_k2_long" : "decode_32x64_k2_long");
     }
     // long K splits over sixteen waves (8 x 4096 x 14336 E2M1: 8.4 us against

@@ -261,9 +261,9 @@ def test_default_variant(lib):
 # MI355X (the host half of the path: validate, pick, launch).
 DEFAULTS = [
     # (is_fp4, M, N, K, variant)
-    (1, 32, 14336, 4096, "decode_32x64_k2"),
-    (1, 16, 14336, 4096, "decode_16x64_k2"),
-    (1, 8, 14336, 4096, "decode_16x64_k2"),
+    (1, 32, 14336, 4096, "decode_32x64"),
+    (1, 16, 14336, 4096, "decode_16x64"),
+    (1, 8, 14336, 4096, "decode_16x64"),
     (1, 1, 14336, 4096, "stream_1x1_k4"),
     (1, 8, 4096, 14336, "stream_1x1_k16"),
     (1, 1, 4096, 14336, "stream_1x1_k16"),
