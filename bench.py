@@ -60,9 +60,10 @@ KERNEL_HEADER = {"stream_": "mx_stream.hpp", "lds_": "mx_lds.hpp", "tile_": "mx_
 
 def kernel_source_digest(kernel_name):
     """sha256 over the sources a kernel is built from (its header, the
-    headers that one includes, and the build flags; the variant's template
-    parameters are in its name): counter-derived traffic figures are only
-    reported for the kernels they were measured on."""
+    headers that one includes, the build flags, and the variant's row of the
+    table in mxgemm.hip, which holds the template parameters that its name
+    does not spell out): counter-derived traffic figures are only reported
+    for the kernels they were measured on."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "block_scaled_precision_mm_amd", "csrc")
@@ -83,6 +84,11 @@ def kernel_source_digest(kernel_name):
     for path in files:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    with open(os.path.join(csrc, "mxgemm.hip")) as f:
+        row = re.compile(r'^\s*MXG_\w+\("%s"' % re.escape(kernel_name))
+        for line in f:
+            if row.match(line):
+                h.update(b"\0" + " ".join(line.split()).encode())
     return h.hexdigest()[:16]
 
 
