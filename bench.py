@@ -495,7 +495,7 @@ def bench_dense(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
