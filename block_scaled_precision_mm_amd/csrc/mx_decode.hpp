@@ -47,7 +47,8 @@
 // of the 8 rows = 128 contiguous bytes) with a padded chunk stride of 160
 // bytes, so both the fragment reads and the staging stores run at full LDS
 // rate; scale codes as [128-K step][row] dwords, so a step's codes of 16
-// consecutive rows are contiguous.
+// consecutive rows are contiguous, with one spare dword after each step (the
+// prologue's lanes that store one row's steps would otherwise share a bank).
 //
 // Ragged M / N: rows past the operand read as zeros (out of the buffer
 // range) and add exactly +0.  K tail: a B stage that runs past the row end
@@ -78,13 +79,16 @@ struct DecodeGeom {
     static constexpr int AGROUP = ACH * CHUNK;               // one 8-row group of A
     static constexpr int NSTEP_MAX = KMAX / 128;
     // LDS map
-    static constexpr int SA_OFF = BM / 8 * AGROUP;                         // [step][BM] dwords
-    static constexpr int SBS_OFF = SA_OFF + NSTEP_MAX * BM * 4;            // [step][BN] dwords
+    // scale codes [step][row] with one spare dword per step: the prologue
+    // stores of one row's steps then fall on different banks
+    static constexpr int SAS = BM + 1, SBSS = BN + 1;                      // step strides (dwords)
+    static constexpr int SA_OFF = BM / 8 * AGROUP;                         // [step][SAS] dwords
+    static constexpr int SBS_OFF = SA_OFF + NSTEP_MAX * SAS * 4;           // [step][SBSS] dwords
     // B slots per wave: two with one wave per row group; one when KS waves
     // share a row group (a wave's LDS operations run in order, so its next
     // stage's stores cannot overtake the reads of the current one)
     static constexpr int SLOTS = KS == 1 ? 2 : 1;
-    static constexpr int B_OFF = SBS_OFF + NSTEP_MAX * BN * 4;             // [wave][SLOTS] slots
+    static constexpr int B_OFF = SBS_OFF + NSTEP_MAX * SBSS * 4;           // [wave][SLOTS] slots
     static constexpr int BYTES = B_OFF + NWT * SLOTS * SLOT;
     // coalesced prologue loads per wave: A chunks (16 bytes)
     static constexpr int PA = cdiv_c(BM * ACH, 64 * NWT);
@@ -95,6 +99,7 @@ struct DecodeGeom {
     // partial tiles of the K parts past the first, summed at the end (in
     // the A region, free by then)
     static_assert((KS - 1) * NW * MT * 64 * 16 <= SA_OFF, "partials must fit the A region");
+    static_assert(B_OFF % 16 == 0, "B slots hold 16-byte pieces");
     static_assert(BM % 8 == 0 && SW % SB == 0 && KMAX % 512 == 0, "tile geometry");
     static_assert(BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     __device__ static constexpr int a_off(int row, int c)
@@ -242,7 +247,7 @@ void mx_gemm_decode(GemmArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (k + e < (unsigned)nst)
-                    *reinterpret_cast<unsigned *>(smem + D::SA_OFF + 4 * ((k + e) * D::BM + row)) = sva[i][e];
+                    *reinterpret_cast<unsigned *>(smem + D::SA_OFF + 4 * ((k + e) * D::SAS + row)) = sva[i][e];
         }
     }
 #pragma unroll
@@ -253,7 +258,7 @@ void mx_gemm_decode(GemmArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (k + e < (unsigned)nst)
-                    *reinterpret_cast<unsigned *>(smem + D::SBS_OFF + 4 * ((k + e) * D::BN + row)) = svb[i][e];
+                    *reinterpret_cast<unsigned *>(smem + D::SBS_OFF + 4 * ((k + e) * D::SBSS + row)) = svb[i][e];
         }
     }
     __syncthreads();   // the A tile and scale codes are shared by all waves
@@ -301,7 +306,7 @@ void mx_gemm_decode(GemmArgs p)
                 fb.d[0] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + g));
                 fb.d[1] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + 4 + g));
             }
-            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::BN + 16 * rw + r)) >> (8 * g);
+            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::SBSS + 16 * rw + r)) >> (8 * g);
             unsigned sa[MT];
 #pragma unroll
             for (int x = 0; x < MT; ++x) {
@@ -312,7 +317,7 @@ void mx_gemm_decode(GemmArgs p)
                     fa[x].d[0] = *reinterpret_cast<const u4v *>(smem + D::a_off(row, 8 * k + g));
                     fa[x].d[1] = *reinterpret_cast<const u4v *>(smem + D::a_off(row, 8 * k + 4 + g));
                 }
-                sa[x] = *reinterpret_cast<const unsigned *>(smem + D::SA_OFF + 4 * (k * D::BM + row)) >> (8 * g);
+                sa[x] = *reinterpret_cast<const unsigned *>(smem + D::SA_OFF + 4 * (k * D::SAS + row)) >> (8 * g);
             }
 #pragma unroll
             for (int x = 0; x < MT; ++x)
