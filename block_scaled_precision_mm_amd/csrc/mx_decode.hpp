@@ -44,11 +44,13 @@
 //     epilogue (bias, activation, 16-bit / FP32 or MX-requantized output).
 //
 // LDS layouts: code rows in groups of 8, chunk-major inside a group (chunk c
-// of the 8 rows = 128 contiguous bytes) with a padded chunk stride of 160
-// bytes, so both the fragment reads and the staging stores run at full LDS
-// rate; scale codes as [128-K step][row] dwords, so a step's codes of 16
-// consecutive rows are contiguous, with one spare dword after each step (the
-// prologue's lanes that store one row's steps would otherwise share a bank).
+// of the 8 rows = 128 contiguous bytes) with a padded chunk stride of 144
+// bytes (36 dwords: the fragment reads take 8 rows of one chunk, the staging
+// stores consecutive chunks of one row, and both land on distinct banks; a
+// stride of 160 put chunks c and c + 4 of a row on the same banks); scale
+// codes as [128-K step][row] dwords, so a step's codes of 16 consecutive rows
+// are contiguous, with one spare dword after each step (the prologue's lanes
+// that store one row's steps would otherwise share a bank).
 //
 // Ragged M / N: rows past the operand read as zeros (out of the buffer
 // range) and add exactly +0.  K tail: a B stage that runs past the row end
@@ -69,7 +71,7 @@ struct DecodeGeom {
     static constexpr int SB = FmtTraits<F>::step_bytes;      // bytes per row per 128-K step
     static constexpr int BM = 16 * MT;                       // A rows
     static constexpr int BN = 16 * NW;                       // B rows (16 per wave)
-    static constexpr int CHUNK = 160;                        // padded 16-byte chunk stride
+    static constexpr int CHUNK = 144;                        // padded 16-byte chunk stride
     static constexpr int SW = 256;                           // B stage: bytes per row
     static constexpr int SPS = SW / SB;                      // MFMA steps per stage
     static constexpr int SCH = SW / 16;                      // chunks per row per stage
