@@ -24,9 +24,10 @@
 //     16-row group of B is streamed by KS waves, wave (w, q) taking rows
 //     [16w, 16w+16) over the q-th of KS equal runs of K -- no barrier in the
 //     K loop; with KS > 1 the KS partial tiles are summed in LDS at the end,
-//     in part order.  Two waves per row group with two-stage rings streamed
-//     32 x 14336 x 4096 faster than one wave with three (a pure read of the
-//     same bytes in that pattern: 6.3 against 7.3 us);
+//     in part order.  With register rings two waves per row group and two
+//     stages streamed 32 x 14336 x 4096 faster than one wave with three (a
+//     pure read of the same bytes in that pattern: 6.3 against 7.3 us); with
+//     the LDS ring below one wave and three slots is as fast or faster;
 //   * the A tile and the scale codes of all the workgroup's rows are loaded
 //     once into LDS (hence the K limit KMAX: the A tile must fit);
 //   * B stages of 256 bytes per row are loaded with 16-byte loads in which
@@ -52,8 +53,10 @@
 // are contiguous, with one spare dword after each step (the prologue's lanes
 // that store one row's steps would otherwise share a bank).
 //
-// Ragged M / N: rows past the operand read as zeros (out of the buffer
-// range) and add exactly +0.  K tail: a B stage that runs past the row end
+// Ragged M / N: B rows past N read as zeros (out of the buffer range) and add
+// exactly +0; A rows past M are neither loaded nor stored into LDS, and as
+// every output row depends on its own A row only, the rows whose LDS holds
+// stale bytes are exactly the ones never written to C.  K tail: a B stage that runs past the row end
 // reads the next row's bytes, so MFMA steps past K are skipped; a row's last
 // 16-byte scale piece may likewise run into the next row (or past the
 // buffer, reading zeros there), and only its dwords below K/128 are kept.
