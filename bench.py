@@ -2,16 +2,25 @@
 """Throughput of the NT MX block-scaled GEMM on one MI355X.
 
 One step = one call of the library's default entry point (one kernel
-launch) on one batch of pre-quantized synthetic input (the pages measure steady-state kernel time
-from already-quantized inputs, excluding compilation and tuning).  Inputs
-are resident in HBM when timing starts; R copies of the operand set are
-rotated so that the rotated footprint (>= 1 GiB) exceeds the 256 MB
-Infinity Cache and every step streams its operands from HBM.
+launch) on one batch of pre-quantized synthetic input: the pages measure
+steady-state kernel time from already-quantized inputs, excluding
+compilation and tuning (devotd.net, section 2; "PyTorch 接上 FlyDSL",
+5ulink.com, paragraph under the support matrix).  Inputs are resident in
+HBM when timing starts; R copies of the operand set are rotated so that the
+rotated footprint (>= 1 GiB) exceeds the 256 MB Infinity Cache and every
+step streams its operands from HBM, and every set is used once before the
+timed region.
+
+The headline workload is the largest one, MXFP4 8192 x 8192 x 8192.  The
+other named workloads (MXFP4 32x256x256, MXFP4 32x14336x4096, MXFP8
+64x4096x4096, MXFP8 and MXFP4 256x28672x8192) are timed in the same process
+and reported under "per_workload", each with its own roofline reading.
 
 Prints one JSON line with the metric, the roofline fraction of the GEMM
 kernel (its average duration from HIP events around the K back-to-back
-launches, on the launch stream) and the CPU oracle's throughput on the host
-as a reference baseline.
+launches, on the launch stream), the shader clock under that load, and the
+CPU oracle's throughput on the host as a reference baseline (all host
+threads, and one thread for the three small workloads).
 """
 from __future__ import annotations
 
@@ -26,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MXFP4/MXFP8 scaled-GEMM TFLOPS on 1 MI355X and % of HBM/MFMA roofline"
-DEFAULT_WORKLOAD = "c2_fp4_32x14336x4096"
+DEFAULT_WORKLOAD = "c5_fp4_8192x8192x8192"
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp4": 10066.0, "fp8": 5033.0}   # dense MXFP4 / MXFP8
 
@@ -40,6 +49,10 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated operand sets (0 = one set, cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-workloads", action="store_true",
+                    help="time only --workload (by default the other named workloads c1-c4 are "
+                         "timed in the same process and reported under per_workload)")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the shader-clock reading under load")
     ap.add_argument("--epilogue", default=None, metavar="ACT,BIAS,OUT",
                     help="time mx_scaled_mm_fused instead: activation none|relu|silu|gelu, "
                          "bias 0|1, output bf16|mxfp8|mxfp4 (e.g. silu,1,mxfp4)")
@@ -53,9 +66,10 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_HEADER = {"stream_": "mx_stream.hpp", "lds_": "mx_lds.hpp", "tile_": "mx_tile.hpp",
+KERNEL_HEADER = {"stream_": "mx_stream.hpp", "tile_": "mx_tile.hpp",
                  "skinny_": "mx_skinny.hpp", "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp",
-                 "gstream_": "mx_stream.hpp", "gtile_": "mx_tile.hpp"}
+                 "gstream_": "mx_stream.hpp", "gtile_": "mx_tile.hpp", "fstream_": "mx_stream.hpp",
+                 "ftile_": "mx_tile.hpp", "fdecode_": "mx_decode.hpp"}
 
 
 def kernel_source_digest(kernel_name):
@@ -85,10 +99,21 @@ def kernel_source_digest(kernel_name):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     with open(os.path.join(csrc, "mxgemm.hip")) as f:
-        row = re.compile(r'^\s*MXG_\w+\("%s"' % re.escape(kernel_name))
-        for line in f:
-            if row.match(line):
-                h.update(b"\0" + " ".join(line.split()).encode())
+        table = f.read()
+    # the variant's row: by its quoted name, or for the stream families by
+    # the macro that spells the name out from its parameters
+    rows = [re.compile(r'^\s*MXG_\w+\("%s"' % re.escape(kernel_name))]
+    m = re.match(r"^(g|f|)stream_(\d+)x(\d+)_k(\d+)$", kernel_name)
+    if m:
+        rows.append(re.compile(r"^\s*MXG_%sSTREAM\(\s*%s,\s*%s,\s*%s\s*\)" % (
+            m.group(1).upper(), m.group(2), m.group(3), m.group(4))))
+        # the register-ring depth those variants are built with
+        rd = re.search(r"constexpr int ring_depth\(.*?\n}\n", table, re.S)
+        if rd:
+            h.update(b"\0" + rd.group(0).encode())
+    for line in table.splitlines():
+        if any(r.match(line) for r in rows):
+            h.update(b"\0" + " ".join(line.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -491,6 +516,230 @@ def bench_dense(args):
                                "sample": "%d of %d rows x %d repetitions, %.2f s" % (rows, M, reps, dt_s)}
     print(json.dumps(out), flush=True)
 
+SUB_WORKLOADS = ("c1_fp4_32x256x256", "c2_fp4_32x14336x4096", "c3_fp8_64x4096x4096",
+                 "c4a_fp8_256x28672x8192", "c4b_fp4_256x28672x8192")
+
+
+def roofline_for(fmt, flops, alg_bytes, ms):
+    """Roofline reading of one launch of `ms` milliseconds: the bound is
+    whichever of bytes / 8 TB/s and FLOPs / dense scaled-MFMA peak is longer."""
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[fmt] * 1e12)
+    if t_hbm >= t_mfma:
+        ach = alg_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[fmt],
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[fmt], 4), "traffic": None}
+    roof["algorithmic_bytes"] = int(alg_bytes)
+    roof["kernel_us"] = round(ms * 1e3, 3)
+    roof["roofline_us"] = round(max(t_hbm, t_mfma) * 1e6, 3)
+    return roof
+
+
+class GemmRunner:
+    """R rotated operand sets of one workload in HBM and a step(i) that
+    enqueues one call of the default entry point (or the fused one) on set
+    i mod R: raw pointers prepared once, so a step is one C ABI call."""
+
+    def __init__(self, mx, cs, rotate_bytes, epilogue=None):
+        import numpy as np
+        import torch
+        dev = torch.device("cuda:0")
+        self.cs = cs
+        is_fp4 = cs.fmt == "fp4"
+        set_bytes = cs.a.nbytes + cs.b.nbytes + cs.sa.nbytes + cs.sb.nbytes + cs.M * cs.N * 2
+        R = 1 if rotate_bytes <= 0 else max(1, math.ceil(rotate_bytes / set_bytes))
+        self.R = R = min(R, 4096)
+        base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (cs.a, cs.b, cs.sa, cs.sb)]
+        self.sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+        self.outs = [torch.empty((cs.M, cs.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        self.stream = torch.cuda.current_stream()
+        st_ptr = self.stream.cuda_stream
+        ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
+                for s_, o in zip(self.sets, self.outs)]
+        self.out_bytes = 2.0                 # bytes of C per output element
+        self.epi = None
+        self.kernel = mx.mx_variant_name(mx.mx_default_variant(is_fp4, cs.M, cs.N, cs.K))
+        if epilogue:
+            act_s, bias_s, out_s = epilogue.split(",")
+            act = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}[act_s]
+            out_kind = {"bf16": 0, "mxfp8": 3, "mxfp4": 4}[out_s]
+            self.bias = (torch.randn(cs.N, device=dev) * 4).to(torch.bfloat16) if bias_s == "1" else None
+            if out_kind >= 3:
+                self.out_bytes = (1.0 if out_kind == 3 else 0.5) + 1.0 / 32
+                c_scales = [torch.empty(cs.M * cs.N // 32, dtype=torch.uint8, device=dev) for _ in range(R)]
+            else:
+                c_scales = [None] * R
+            self.c_scales = c_scales
+            fused = mx._lib.mx_scaled_mm_fused
+            bias_ptr = self.bias.data_ptr() if self.bias is not None else None
+            csp = [t.data_ptr() if t is not None else None for t in c_scales]
+            self.epi = {"act": act_s, "bias": bias_s == "1", "out": out_s}
+            self.kernel = mx.mx_fused_variant_name(mx.mx_fused_default_variant(is_fp4, cs.M, cs.N, cs.K))
+
+            def step(i):
+                a, b, sa, sb, c = ptrs[i % R]
+                rc = fused(1 if is_fp4 else 0, a, b, sa, sb, bias_ptr, act, c, csp[i % R], cs.M, cs.N,
+                           cs.K, out_kind, -1, st_ptr)
+                if rc:
+                    raise mx.MxGemmError(rc, "bench step")
+        else:
+            entry = mx._lib.mx_scaled_mm_fp4 if is_fp4 else mx._lib.mx_scaled_mm_fp8
+
+            def step(i):
+                a, b, sa, sb, c = ptrs[i % R]
+                rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
+                if rc:
+                    raise mx.MxGemmError(rc, "bench step")
+        self.step = step
+        self.alg_bytes = cs.algorithmic_bytes(2) - cs.M * cs.N * (2.0 - self.out_bytes)
+
+    def time(self, steps, warmup):
+        """W warm-up steps, then one call on every rotated set (so that no
+        timed step is the first touch of its set), then exactly `steps`
+        back-to-back timed steps between two HIP events on the launch stream.
+        Returns (ms per step, host enqueue seconds, wall seconds)."""
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        for i in range(self.R):
+            self.step(i)
+        torch.cuda.synchronize()
+        # Keep the GPU busy with unrelated work while the host enqueues the
+        # timed steps, so that no step waits for the host: the timed region
+        # holds `steps` back-to-back launches, bracketed by two events on
+        # the launch stream.
+        filler = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        for _ in range(max(8, steps // 4)):
+            filler.add_(1.0)
+        t0 = time.perf_counter()
+        ev0.record(self.stream)
+        for i in range(steps):
+            self.step(i)
+        ev1.record(self.stream)
+        t_enqueue = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del filler
+        return ev0.elapsed_time(ev1) / steps, t_enqueue, wall
+
+    def roofline(self, ms, workload):
+        cs = self.cs
+        roof = roofline_for(cs.fmt, cs.flops, self.alg_bytes, ms)
+        roof["kernel"] = self.kernel
+        rec = recorded_traffic(workload, self.kernel) if self.epi is None else None
+        if rec is not None:
+            roof["traffic"] = rec["hbm_bytes_per_launch"]
+            roof["traffic_unit"] = "bytes/launch"
+            roof["traffic_vs_algorithmic"] = round(rec["hbm_bytes_per_launch"] / self.alg_bytes, 3)
+        return roof
+
+
+def dispatch_floor(mx, cs, steps):
+    """Time of an empty kernel on the same grid as the workload's default
+    kernel, back to back (the launch cost every call pays)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    is_fp4 = 1 if cs.fmt == "fp4" else 0
+    fn = mx._lib.mx_empty_like
+    for _ in range(20):
+        fn(is_fp4, cs.M, cs.N, cs.K, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        rc = fn(is_fp4, cs.M, cs.N, cs.K, stream.cuda_stream)
+        if rc:
+            raise mx.MxGemmError(rc, "mx_empty_like")
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def read_sclk():
+    """Current shader clock of GPU 0 in MHz from rocm-smi, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+    except Exception:
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line.lower():
+            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+def sclk_under_load(runner, ms_per_step, seconds=3.0):
+    """Shader clock sampled while the headline kernel runs back to back for
+    about `seconds` (the MFMA-heavy kernels run below the 2.4 GHz peak)."""
+    import threading
+    import torch
+    n = max(1, int(seconds / (ms_per_step * 1e-3)))
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.3)
+        while not stop.is_set() and len(samples) < 4:
+            v = read_sclk()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    for i in range(n):
+        runner.step(i)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    idle = read_sclk()
+    return {"under_load_mhz": samples, "after_mhz": idle, "source": "rocm-smi --showclocks",
+            "load": "%d back-to-back calls (%.1f s)" % (n, n * ms_per_step * 1e-3)}
+
+
+def cpu_single_thread(names, budget_s):
+    """The oracle on one host thread (OMP_NUM_THREADS=1, in a child process)
+    for the small workloads: seconds per whole workload, from a bounded
+    block of output rows."""
+    import subprocess
+    code = r"""
+import json, sys, time
+sys.path.insert(0, %r)
+import mxgen, oracle
+out = {}
+for name in %r:
+    cs = mxgen.case(name)
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.gemm(cs.fmt, cs.a[:1], cs.b, cs.sa[:1], cs.sb, 1, cs.N, cs.K)
+    t_row = max(time.perf_counter() - t0, 1e-6)
+    rows = int(max(1, min(cs.M, %f / t_row)))
+    t0 = time.perf_counter()
+    oracle.gemm(cs.fmt, cs.a[:rows], cs.b, cs.sa[:rows], cs.sb, rows, cs.N, cs.K)
+    dt = time.perf_counter() - t0
+    out[name] = {"seconds_per_workload": dt * cs.M / rows,
+                 "value": 2.0 * rows * cs.N * cs.K / dt / 1e12, "unit": "TFLOP/s",
+                 "sample": "%%d of %%d output rows" %% (rows, cs.M)}
+print(json.dumps(out))
+""" % (ROOT, list(names), budget_s)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-500:]}
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    res["cores"] = 1
+    return res
+
 
 def main():
     args = parse()
@@ -510,119 +759,35 @@ def main():
     if args.workload.startswith("g"):
         bench_grouped(args)
         return
-    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
     import torch
 
     import mxgen
     import block_scaled_precision_mm_amd as mx
 
     torch.cuda.set_device(0)
-    cs = mxgen.case(args.workload)
+    subs = [] if args.no_sub_workloads else [w for w in SUB_WORKLOADS if w != args.workload]
+    # input generation is numpy work that releases the GIL: build the
+    # workloads side by side
+    with ThreadPoolExecutor(max_workers=1 + len(subs)) as ex:
+        futs = {name: ex.submit(mxgen.case, name) for name in [args.workload] + subs}
+        cases = {name: f.result() for name, f in futs.items()}
+
+    cs = cases[args.workload]
+    runner = GemmRunner(mx, cs, args.rotate_bytes, args.epilogue)
+    ms, t_enqueue, wall = runner.time(args.steps, args.warmup)
+    roof = runner.roofline(ms, args.workload)
+    tflops = cs.flops / (ms * 1e-3) / 1e12
     is_fp4 = cs.fmt == "fp4"
-    dev = torch.device("cuda:0")
-    set_bytes = cs.a.nbytes + cs.b.nbytes + cs.sa.nbytes + cs.sb.nbytes + cs.M * cs.N * 2
-    R = 1 if args.rotate_bytes <= 0 else max(1, math.ceil(args.rotate_bytes / set_bytes))
-    R = min(R, 4096)
-    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (cs.a, cs.b, cs.sa, cs.sb)]
-    sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
-    outs = [torch.empty((cs.M, cs.N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-    variant = mx.mx_default_variant(is_fp4, cs.M, cs.N, cs.K)
-    stream = torch.cuda.current_stream()
-    # raw pointers, prepared once: each timed step is one C ABI call
-    entry = mx._lib.mx_scaled_mm_fp4 if is_fp4 else mx._lib.mx_scaled_mm_fp8
-    ptrs = [(s_[0].data_ptr(), s_[1].data_ptr(), s_[2].data_ptr(), s_[3].data_ptr(), o.data_ptr())
-            for s_, o in zip(sets, outs)]
-    st_ptr = stream.cuda_stream
-    out_bytes = 2.0                 # bytes of C per output element
-    epi = None
-    if args.epilogue:
-        act_s, bias_s, out_s = args.epilogue.split(",")
-        act = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}[act_s]
-        out_kind = {"bf16": 0, "mxfp8": 3, "mxfp4": 4}[out_s]
-        bias = (torch.randn(cs.N, device=dev) * 4).to(torch.bfloat16) if bias_s == "1" else None
-        if out_kind >= 3:
-            out_bytes = (1.0 if out_kind == 3 else 0.5) + 1.0 / 32
-            c_scales = [torch.empty(cs.M * cs.N // 32, dtype=torch.uint8, device=dev) for _ in range(R)]
-        else:
-            c_scales = [None] * R
-        fused = mx._lib.mx_scaled_mm_fused
-        bias_ptr = bias.data_ptr() if bias is not None else None
-        csp = [t.data_ptr() if t is not None else None for t in c_scales]
-        epi = {"act": act_s, "bias": bias_s == "1", "out": out_s}
-
-        def step(i):
-            a, b, sa, sb, c = ptrs[i % R]
-            rc = fused(1 if is_fp4 else 0, a, b, sa, sb, bias_ptr, act, c, csp[i % R], cs.M, cs.N, cs.K,
-                       out_kind, -1, st_ptr)
-            if rc:
-                raise mx.MxGemmError(rc, "bench step")
-    else:
-        def step(i):
-            a, b, sa, sb, c = ptrs[i % R]
-            rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
-            if rc:
-                raise mx.MxGemmError(rc, "bench step")
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Keep the GPU busy with unrelated work while the host enqueues the timed
-    # steps, so that no step waits for the host: the timed region then holds
-    # K back-to-back launches of the GEMM on `stream`, bracketed by two HIP
-    # events recorded on that same stream.
-    filler = torch.empty(256 << 20, dtype=torch.float32, device=dev)
-    K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    for _ in range(max(8, K // 4)):
-        filler.add_(1.0)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        step(args.warmup + i)
-    ev1.record(stream)
-    t_enqueue = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    span_ms = ev0.elapsed_time(ev1)
-    ms_per_step = span_ms / K
-    kern_ms = ms_per_step          # one GEMM launch per step
-    del filler
-
-    flops = cs.flops
-    alg_bytes = cs.algorithmic_bytes(2) - cs.M * cs.N * (2.0 - out_bytes)
-    tflops = flops / (ms_per_step * 1e-3) / 1e12
-    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops / (MFMA_PEAK_TFLOPS[cs.fmt] * 1e12)
-    if t_hbm >= t_mfma:
-        achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        achieved = flops / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[cs.fmt],
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[cs.fmt], 4), "traffic": None}
-    roof["kernel"] = mx.mx_variant_name(variant)
-    if epi is not None:
-        roof["kernel"] = mx.mx_fused_variant_name(mx.mx_fused_default_variant(is_fp4, cs.M, cs.N, cs.K))
-    rec = recorded_traffic(args.workload, roof["kernel"]) if epi is None else None
-    if rec is not None:
-        roof["traffic"] = rec["hbm_bytes_per_launch"]
-        roof["traffic_unit"] = "bytes/launch"
-        roof["traffic_vs_algorithmic"] = round(rec["hbm_bytes_per_launch"] / alg_bytes, 3)
-    roof["algorithmic_bytes"] = int(alg_bytes)
-    roof["kernel_us"] = round(kern_ms * 1e3, 3)
-    roof["roofline_us"] = round(max(t_hbm, t_mfma) * 1e6, 3)
-
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -631,14 +796,47 @@ def main():
         "config": {"workload": args.workload, "M": cs.M, "N": cs.N, "K": cs.K,
                    "operands": "MXFP4 (E2M1) + E8M0/32" if is_fp4 else "MXFP8 (E4M3) + E8M0/32",
                    "accumulate": "fp32", "out": "bf16", "layout": "NT", "recipe": cs.recipe,
-                   "rotating_sets": R, "variant": roof["kernel"],
-                   "epilogue": epi},
+                   "rotating_sets": runner.R, "variant": runner.kernel, "epilogue": runner.epi},
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_s": round(t_enqueue, 4),
     }
+    if not args.no_sclk:
+        out["sclk"] = sclk_under_load(runner, ms)
+        load = out["sclk"]["under_load_mhz"]
+        if load and roof["bound"] == "mfma":
+            f = min(load) / 2400.0
+            roof["peak_at_sclk"] = round(roof["peak"] * f, 1)
+            roof["frac_at_sclk"] = round(roof["achieved"] / roof["peak_at_sclk"], 4)
+    del runner
+    torch.cuda.empty_cache()
+
+    # the other named workloads, each timed the same way in this process
+    per = {}
+    for name in subs:
+        sc = cases[name]
+        r = GemmRunner(mx, sc, args.rotate_bytes)
+        steps = max(100, 2 * r.R) if sc.M * sc.N > 32 * 256 else 2000
+        sms, _, _ = r.time(steps, 10)
+        rec = {"us_per_call": round(sms * 1e3, 3),
+               "value": round(sc.flops / (sms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+               "steps": steps, "rotating_sets": r.R, "recipe": sc.recipe,
+               "roofline": r.roofline(sms, name)}
+        if name.startswith("c1_"):
+            # launch-bound: its roofline time is ns; the reading that means
+            # something is how close it runs to an empty launch on its grid
+            fl = dispatch_floor(mx, sc, steps)
+            rec["dispatch_floor_us"] = round(fl * 1e3, 3)
+            rec["dispatch_floor_frac"] = round(fl / sms, 4)
+        per[name] = rec
+        del r
+        torch.cuda.empty_cache()
+    if per:
+        out["per_workload"] = per
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cs, args.cpu_seconds)
+        small = [w for w in ("c1_fp4_32x256x256", "c2_fp4_32x14336x4096", "c3_fp8_64x4096x4096")]
+        out["cpu_baseline"]["one_thread"] = cpu_single_thread(small, 2.0)
     print(json.dumps(out), flush=True)
 
 

@@ -65,11 +65,12 @@ _lib.mx_fused_default_variant.argtypes = [_INT, _I64, _I64, _I64]
 _lib.mx_fused_variant_max_k.argtypes = [_INT, _INT]
 _lib.mx_fused_variant_max_k.restype = _I64
 _lib.mx_dense_gemm.argtypes = [_INT, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
+_lib.mx_empty_like.argtypes = [_INT, _I64, _I64, _I64, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
-           "mx_fused_num_variants", "mx_fused_default_variant", "mx_dense_gemm"):
+           "mx_fused_num_variants", "mx_fused_default_variant", "mx_dense_gemm", "mx_empty_like"):
     getattr(_lib, _f).restype = _INT
 
 # every symbol include/mxgemm.h declares
@@ -79,7 +80,7 @@ EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_variant_name", "mx_grouped_default_variant",
            "mx_scaled_mm_fused", "mx_fused_num_variants", "mx_fused_variant_name",
-           "mx_fused_default_variant", "mx_fused_variant_max_k", "mx_dense_gemm")
+           "mx_fused_default_variant", "mx_fused_variant_max_k", "mx_dense_gemm", "mx_empty_like")
 
 
 class MxGemmError(RuntimeError):
@@ -349,3 +350,11 @@ def scaled_mm(a, b, a_scale, b_scale, fmt: str, M: int, N: int, K: int,
     fn = mx_scaled_mm_fp4 if fmt == "fp4" else mx_scaled_mm_fp8
     fn(a, b, a_scale, b_scale, c, M, N, K, stream=stream)
     return c
+
+
+def mx_empty_like(is_fp4, M, N, K, stream=None) -> None:
+    """Enqueue an empty kernel on the grid the default product would use for
+    this shape (C ABI mx_empty_like; measurement of the launch cost)."""
+    st = _lib.mx_empty_like(int(bool(is_fp4)), M, N, K, _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_empty_like")

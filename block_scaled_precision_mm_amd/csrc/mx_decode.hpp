@@ -63,7 +63,7 @@
 #pragma once
 
 #include "mx_epilogue.hpp"
-#include "mx_lds.hpp"
+#include "mx_sync.hpp"
 #include "mx_tile.hpp"
 
 namespace mxg {

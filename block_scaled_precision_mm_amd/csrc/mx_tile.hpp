@@ -63,7 +63,7 @@
 
 #include "mx_epilogue.hpp"
 #include "mx_group.hpp"
-#include "mx_lds.hpp"
+#include "mx_sync.hpp"
 
 namespace mxg {
 

@@ -268,6 +268,15 @@ int mx_dense_gemm(int dtype, int trans_a, int trans_b, const void *a, const void
  * negative status for an invalid shape. */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
 
+/* Measurement support: enqueue an empty kernel on exactly the grid and
+ * workgroup size that mx_scaled_mm_fp4/fp8 would launch for this shape, so
+ * that the launch cost alone can be timed next to the product (the
+ * "dispatch floor" of shapes too small to reach any bandwidth or MFMA
+ * roofline).  Returns MXG_OK after enqueueing, or the status
+ * mx_default_variant gives for the shape, MXG_ERR_DEVICE or MXG_ERR_HIP.
+ * Touches no memory. */
+int mx_empty_like(int is_fp4, int64_t M, int64_t N, int64_t K, mxg_stream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char *mx_status_string(int status);
 

@@ -50,3 +50,21 @@ def test_bad_quant_workload_names(name):
 
 def test_quant_workload_name():
     assert bench.parse_quant_workload("quant_fp8_8192x8192") == ("fp8", 8192, 8192)
+
+
+def test_digest_separates_stream_variants():
+    # the stream families carry no quoted name in the variant table: their
+    # rows are found from the parameters the name spells out
+    d = {n: bench.kernel_source_digest(n) for n in ("stream_2x2_k4", "gstream_1x2_k4", "stream_4x2_k8",
+                                                    "stream_2x4_k8", "fstream_2x4_k8")}
+    assert len(set(d.values())) == len(d)
+
+
+def test_roofline_reading():
+    # c2's bytes at 4.023 us are exactly the HBM roofline; c5's FLOPs at the
+    # dense MXFP4 peak are the MFMA roofline
+    r = bench.roofline_for("fp4", 2.0 * 32 * 14336 * 4096, 32182272.0, 32182272.0 / 8e12 * 1e3)
+    assert r["bound"] == "hbm" and abs(r["frac"] - 1.0) < 1e-3
+    fl = 2.0 * 8192 ** 3
+    r = bench.roofline_for("fp4", fl, 205.5e6, fl / 10066e12 * 1e3 * 2)
+    assert r["bound"] == "mfma" and abs(r["frac"] - 0.5) < 1e-3

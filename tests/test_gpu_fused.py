@@ -6,10 +6,11 @@ C ABI) against the oracle's product + epilogue reference.
   SiLU / tanh-GELU); this is the product's pre-rounding bound carried
   through the activation.
 * BF16 / FP16 output: bit-exact RNE of the same variant's FP32 output.
-* MX output: bit-exact equal to mx_quantize_bf16 applied to the same
-  variant's BF16 output (the documented definition), and every dequantized
-  element within the MX format's worst rounding / saturation step of its
-  block (2 * 2^(s-127) for E2M1, 64 * 2^(s-127) for E4M3) plus the FP32
+* MX output: bit-exact equal to the oracle's quantizer (oracle.quantize,
+  pinned on its own in test_oracle_quant.py) applied to the same variant's
+  BF16 output -- the documented definition -- and to mx_quantize_bf16 of
+  it; every dequantized element within the MX format's worst rounding /
+  saturation step of its block (2 * 2^(s-127) for E2M1, 64 * 2^(s-127) for E4M3) plus the FP32
   bound of y_ref.
 """
 from __future__ import annotations
@@ -92,6 +93,11 @@ def check_case(mx, fmt, M, N, K, act, with_bias, variant, seed):
         mx.mx_quantize_bf16(cb, qc, qs, M, N, qf == "fp4")
         torch.cuda.synchronize()
         assert torch.equal(codes, qc) and torch.equal(scales, qs), what + " MX output != quantize(BF16 output)"
+        # and the oracle's quantizer of the same BF16 output, bit for bit
+        cb_bits = cb.view(torch.int16).cpu().numpy().view(np.uint16)
+        oc, osc = oracle.quantize(qf, cb_bits, M, N)
+        assert np.array_equal(codes.cpu().numpy().reshape(oc.shape), oc), what + " MX codes != oracle.quantize"
+        assert np.array_equal(scales.cpu().numpy().reshape(osc.shape), osc), what + " MX scales != oracle.quantize"
         # dequantized output against the reference
         vals = refdecode.values(qf, codes.cpu().numpy().reshape(M, -1), M, N)
         sc = scales.cpu().numpy().reshape(M, N // 32).astype(np.int64)
