@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--epilogue", default=None, metavar="ACT,BIAS,OUT",
                     help="time mx_scaled_mm_fused instead: activation none|relu|silu|gelu, "
                          "bias 0|1, output bf16|mxfp8|mxfp4 (e.g. silu,1,mxfp4)")
+    ap.add_argument("--config", default=None, metavar="VARIANT[:PARTS]",
+                    help="force a kernel variant (by name) and K-part count instead of the default")
     ap.add_argument("--variant", type=int, default=None,
                     help="grouped workloads: kernel variant index (default: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -544,7 +546,7 @@ class GemmRunner:
     enqueues one call of the default entry point (or the fused one) on set
     i mod R: raw pointers prepared once, so a step is one C ABI call."""
 
-    def __init__(self, mx, cs, rotate_bytes, epilogue=None):
+    def __init__(self, mx, cs, rotate_bytes, epilogue=None, config=None):
         import numpy as np
         import torch
         dev = torch.device("cuda:0")
@@ -562,7 +564,16 @@ class GemmRunner:
                 for s_, o in zip(self.sets, self.outs)]
         self.out_bytes = 2.0                 # bytes of C per output element
         self.epi = None
-        self.kernel = mx.mx_variant_name(mx.mx_default_variant(is_fp4, cs.M, cs.N, cs.K))
+        variant, self.splits = mx.mx_default_config(is_fp4, cs.M, cs.N, cs.K)
+        if config:
+            name, _, sp = config.partition(":")
+            variant = next(v for v in range(mx.mx_num_variants()) if mx.mx_variant_name(v) == name)
+            self.splits = int(sp or 1)
+        self.kernel = mx.mx_variant_name(variant)
+        # the split-K workspace (zero-filled once; every call leaves it ready)
+        ws_bytes = mx.mx_config_workspace_bytes(variant, self.splits, cs.M, cs.N)
+        self.ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        ws_ptr = self.ws.data_ptr() if ws_bytes else None
         if epilogue:
             act_s, bias_s, out_s = epilogue.split(",")
             act = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}[act_s]
@@ -586,12 +597,21 @@ class GemmRunner:
                            cs.K, out_kind, -1, st_ptr)
                 if rc:
                     raise mx.MxGemmError(rc, "bench step")
+        elif config:
+            cfg = mx._lib.mx_scaled_mm_config
+
+            def step(i):
+                a, b, sa, sb, c = ptrs[i % R]
+                rc = cfg(1 if is_fp4 else 0, a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, variant, self.splits,
+                         ws_ptr, ws_bytes, st_ptr)
+                if rc:
+                    raise mx.MxGemmError(rc, "bench step")
         else:
             entry = mx._lib.mx_scaled_mm_fp4 if is_fp4 else mx._lib.mx_scaled_mm_fp8
 
             def step(i):
                 a, b, sa, sb, c = ptrs[i % R]
-                rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, st_ptr)
+                rc = entry(a, b, sa, sb, c, cs.M, cs.N, cs.K, 0, ws_ptr, ws_bytes, st_ptr)
                 if rc:
                     raise mx.MxGemmError(rc, "bench step")
         self.step = step
@@ -632,6 +652,7 @@ class GemmRunner:
         cs = self.cs
         roof = roofline_for(cs.fmt, cs.flops, self.alg_bytes, ms)
         roof["kernel"] = self.kernel
+        roof["k_parts"] = self.splits
         rec = recorded_traffic(workload, self.kernel) if self.epi is None else None
         if rec is not None:
             roof["traffic"] = rec["hbm_bytes_per_launch"]
@@ -775,7 +796,7 @@ def main():
         cases = {name: f.result() for name, f in futs.items()}
 
     cs = cases[args.workload]
-    runner = GemmRunner(mx, cs, args.rotate_bytes, args.epilogue)
+    runner = GemmRunner(mx, cs, args.rotate_bytes, args.epilogue, args.config)
     ms, t_enqueue, wall = runner.time(args.steps, args.warmup)
     roof = runner.roofline(ms, args.workload)
     tflops = cs.flops / (ms * 1e-3) / 1e12
@@ -796,7 +817,8 @@ def main():
         "config": {"workload": args.workload, "M": cs.M, "N": cs.N, "K": cs.K,
                    "operands": "MXFP4 (E2M1) + E8M0/32" if is_fp4 else "MXFP8 (E4M3) + E8M0/32",
                    "accumulate": "fp32", "out": "bf16", "layout": "NT", "recipe": cs.recipe,
-                   "rotating_sets": runner.R, "variant": runner.kernel, "epilogue": runner.epi},
+                   "rotating_sets": runner.R, "variant": runner.kernel, "k_parts": runner.splits,
+                   "epilogue": runner.epi},
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_s": round(t_enqueue, 4),

@@ -4,9 +4,12 @@ Argument marshalling only: every step of the product runs in the HIP
 kernels of ``csrc/``.  PyTorch supplies device memory and the stream.  The
 functions carry the C ABI's names (see ``include/mxgemm.h``):
 
-    mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None)
+    mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace="auto", stream=None)
     mx_scaled_mm_fp8(...)
-    mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, out_dtype=None, stream=None)
+    mx_scaled_mm_workspace_bytes(is_fp4, M, N, K)
+    mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, splits=1,
+                        workspace="auto", out_dtype=None, stream=None)
+    mx_default_config(is_fp4, M, N, K, with_workspace=True) -> (variant, splits)
     mx_default_variant(is_fp4, M, N, K)
 
 ``a``/``b`` are contiguous 1-byte CUDA tensors holding packed codes
@@ -41,9 +44,14 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _INT = ctypes.c_int
-_lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
+_lib.mx_scaled_mm_fp4.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]
 _lib.mx_scaled_mm_fp8.argtypes = _lib.mx_scaled_mm_fp4.argtypes
-_lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P]
+_lib.mx_scaled_mm_config.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _SZ, _P]
+_lib.mx_scaled_mm_workspace_bytes.argtypes = [_INT, _I64, _I64, _I64]
+_lib.mx_scaled_mm_workspace_bytes.restype = _SZ
+_lib.mx_config_workspace_bytes.argtypes = [_INT, _INT, _I64, _I64]
+_lib.mx_config_workspace_bytes.restype = _SZ
+_lib.mx_default_config.argtypes = [_INT, _I64, _I64, _I64, _INT, ctypes.POINTER(_INT)]
 _lib.mx_default_variant.argtypes = [_INT, _I64, _I64, _I64]
 _lib.mx_variant_max_k.argtypes = [_INT, _INT]
 _lib.mx_variant_max_k.restype = _I64
@@ -67,6 +75,7 @@ _lib.mx_fused_variant_max_k.restype = _I64
 _lib.mx_dense_gemm.argtypes = [_INT, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
 _lib.mx_empty_like.argtypes = [_INT, _I64, _I64, _I64, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
+           "mx_default_config",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
@@ -75,6 +84,7 @@ for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
 
 # every symbol include/mxgemm.h declares
 EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
+           "mx_scaled_mm_workspace_bytes", "mx_config_workspace_bytes", "mx_default_config",
            "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
            "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
@@ -131,29 +141,75 @@ def _out_code(c, out_dtype):
     raise ValueError("out_dtype is required when c is a raw pointer")
 
 
-def mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None) -> None:
-    _check_tensors(True, a, b, a_scale, b_scale, c, M, N, K)
-    st = _lib.mx_scaled_mm_fp4(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
-                               _out_code(c, out_dtype), _stream(stream))
+_WORKSPACES = {}
+
+
+def _workspace(ws, nbytes, stream_ptr):
+    """(pointer, bytes) of the split-K workspace argument (see the module doc)."""
+    if ws is None or nbytes == 0:
+        return 0, 0
+    if isinstance(ws, torch.Tensor):
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor")
+        return ws.data_ptr(), ws.numel() * ws.element_size()
+    if ws != "auto":
+        raise ValueError("workspace must be a tensor, None or 'auto'")
+    key = (torch.cuda.current_device(), stream_ptr)
+    t = _WORKSPACES.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        _WORKSPACES[key] = t
+    return t.data_ptr(), t.numel()
+
+
+def mx_scaled_mm_workspace_bytes(is_fp4, M, N, K) -> int:
+    return int(_lib.mx_scaled_mm_workspace_bytes(int(bool(is_fp4)), M, N, K))
+
+
+def mx_config_workspace_bytes(variant, splits, M, N) -> int:
+    return int(_lib.mx_config_workspace_bytes(variant, splits, M, N))
+
+
+def _default(is_fp4, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, stream, fn, name):
+    _check_tensors(is_fp4, a, b, a_scale, b_scale, c, M, N, K)
+    st_ptr = _stream(stream)
+    wp, wb = _workspace(workspace, mx_scaled_mm_workspace_bytes(is_fp4, M, N, K), st_ptr)
+    st = fn(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K, _out_code(c, out_dtype),
+            wp, wb, st_ptr)
     if st:
-        raise MxGemmError(st, "mx_scaled_mm_fp4")
+        raise MxGemmError(st, name)
 
 
-def mx_scaled_mm_fp8(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None) -> None:
-    _check_tensors(False, a, b, a_scale, b_scale, c, M, N, K)
-    st = _lib.mx_scaled_mm_fp8(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(c), M, N, K,
-                               _out_code(c, out_dtype), _stream(stream))
-    if st:
-        raise MxGemmError(st, "mx_scaled_mm_fp8")
+def mx_scaled_mm_fp4(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace="auto",
+                     stream=None) -> None:
+    _default(True, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, stream,
+             _lib.mx_scaled_mm_fp4, "mx_scaled_mm_fp4")
 
 
-def mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, out_dtype=None,
-                        stream=None) -> None:
+def mx_scaled_mm_fp8(a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, workspace="auto",
+                     stream=None) -> None:
+    _default(False, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, stream,
+             _lib.mx_scaled_mm_fp8, "mx_scaled_mm_fp8")
+
+
+def mx_scaled_mm_config(is_fp4, a, b, a_scale, b_scale, c, M, N, K, variant, splits=1,
+                        workspace="auto", out_dtype=None, stream=None) -> None:
     _check_tensors(bool(is_fp4), a, b, a_scale, b_scale, c, M, N, K)
+    st_ptr = _stream(stream)
+    wp, wb = _workspace(workspace, mx_config_workspace_bytes(variant, splits, M, N), st_ptr)
     st = _lib.mx_scaled_mm_config(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
-                                  _ptr(c), M, N, K, _out_code(c, out_dtype), variant, _stream(stream))
+                                  _ptr(c), M, N, K, _out_code(c, out_dtype), variant, splits, wp, wb, st_ptr)
     if st:
         raise MxGemmError(st, "mx_scaled_mm_config")
+
+
+def mx_default_config(is_fp4, M, N, K, with_workspace=True):
+    """(variant, K parts) of the default entry points for this shape."""
+    sp = _INT(0)
+    v = int(_lib.mx_default_config(int(bool(is_fp4)), M, N, K, int(bool(with_workspace)), ctypes.byref(sp)))
+    if v < 0:
+        raise MxGemmError(v, "mx_default_config")
+    return v, int(sp.value)
 
 
 def mx_default_variant(is_fp4, M, N, K) -> int:

@@ -67,9 +67,15 @@ struct GemmArgs {
     const uint8_t *a, *b, *sa, *sb;
     void *c;
     int M, N;
-    int nsteps;           // K / 128
-    unsigned row_bytes;   // packed bytes per operand row: K/2 (FP4) or K (FP8)
-    unsigned srow_bytes;  // scale bytes per row: K/32
+    int nsteps;           // 128-K steps this workgroup multiplies over: K / 128, or its K part's
+    unsigned row_bytes;   // row stride of the packed operands: K/2 (FP4) or K (FP8) bytes
+    unsigned srow_bytes;  // row stride of the scales: K/32 bytes
+    unsigned kbytes;      // packed bytes per row in this workgroup's K range (row_bytes without split-K)
+    // split-K across workgroups (mx_splitk.hpp): number of K parts
+    // (gridDim.z), FP32 partial tiles and per-tile arrival counters
+    int splits;
+    float *ws;
+    unsigned *flags;
     // grouped products only (mx_group.hpp): end offset of each group's rows
     // of A and C, and the group count; B and its scales hold one [N][K]
     // operand per group

@@ -44,6 +44,7 @@
 #include "mx_common.hpp"
 #include "mx_epilogue.hpp"
 #include "mx_group.hpp"
+#include "mx_splitk.hpp"
 
 namespace mxg {
 
@@ -151,17 +152,22 @@ void mx_gemm_stream(GemmArgs p)
         m0 = local * (16 * MT);
     }
     const int n0 = blockIdx.x * (16 * WN);
+    // split-K across workgroups: this workgroup's K part (whole groups)
+    if constexpr (!GRP && !EPI)
+        select_split<F>(p, 4);
 
-    // Buffers over this workgroup's rows only: rows past M or N fall
-    // outside the range and read as zeros.
+    // Buffers over this workgroup's rows (and K part) only: rows past M or
+    // N fall outside the range and read as zeros.
     const int mrows = min(16 * MT, p.M - m0);
     const int nrows = min(16 * WN, p.N - n0);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * p.row_bytes, mrows * p.row_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * p.row_bytes, nrows * p.row_bytes);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.a + (size_t)m0 * p.row_bytes, part_range(mrows, p.row_bytes, p.kbytes));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.b + (size_t)n0 * p.row_bytes, part_range(nrows, p.row_bytes, p.kbytes));
     const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
+        make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, part_range(mrows, p.srow_bytes, 4u * p.nsteps));
     const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
+        make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, part_range(nrows, p.srow_bytes, 4u * p.nsteps));
     StreamOffsets<MT, WN> o;
 #pragma unroll
     for (int x = 0; x < MT; ++x)
@@ -274,6 +280,40 @@ void mx_gemm_stream(GemmArgs p)
             for (int y = 0; y < WN; ++y)
                 *reinterpret_cast<v4f *>(&red[kw][16 * x + r][16 * y + 4 * g]) = acc[x][y];
         __syncthreads();
+        if constexpr (!GRP && !EPI) {
+            if (p.splits > 1) {
+                // split-K: this part's tile (its KW partials summed in wave
+                // order), then the parts summed by the last to finish
+                constexpr int CG = 4 * WN, NQ = 16 * MT * CG, NTH = 64 * KW;
+                constexpr int QPT = (NQ + NTH - 1) / NTH;
+                const int tid = (int)threadIdx.x;
+                v4f fin[QPT];
+#pragma unroll
+                for (int i = 0; i < QPT; ++i) {
+                    const int q = tid + i * NTH;
+                    v4f sum = {0.f, 0.f, 0.f, 0.f};
+                    if (q < NQ) {
+                        sum = *reinterpret_cast<const v4f *>(&red[0][q / CG][4 * (q % CG)]);
+#pragma unroll
+                        for (int w = 1; w < KW; ++w)
+                            sum += *reinterpret_cast<const v4f *>(&red[w][q / CG][4 * (q % CG)]);
+                    }
+                    fin[i] = sum;
+                }
+                const int tile = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+                if (!splitk_reduce<QPT, NTH>(p, tile, tid, [&](int j) { return fin[j]; },
+                                             [&](int j, v4f x) { fin[j] = x; }))
+                    return;
+#pragma unroll
+                for (int i = 0; i < QPT; ++i) {
+                    const int q = tid + i * NTH;
+                    const int m = m0 + q / CG, n = n0 + 4 * (q % CG);
+                    if (q < NQ && m < p.M && n < p.N)
+                        store4<OUT>(p.c, p.N, m, n, fin[i], vec_ok && n + 3 < p.N);
+                }
+                return;
+            }
+        }
         // the KW partials summed in wave order while the output is written
         store_reduced_tile<OUT, EPI, 16 * MT, 4 * WN>(
             p, m0, n0, (int)threadIdx.x, 64 * KW, [&](int row, int c4) {

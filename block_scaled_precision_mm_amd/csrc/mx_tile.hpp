@@ -63,6 +63,7 @@
 
 #include "mx_epilogue.hpp"
 #include "mx_group.hpp"
+#include "mx_splitk.hpp"
 #include "mx_sync.hpp"
 
 namespace mxg {
@@ -213,18 +214,23 @@ void mx_gemm_tile(GemmArgs p)
         tn = local / nbm;
     } else {
         tile_of(blockIdx.x, (p.M + G::BM - 1) / G::BM, nbn, tm, tn);
+        // split-K: this workgroup's K part (whole periods of four steps)
+        if constexpr (!EPI)
+            select_split<F>(p, 4);
     }
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int mrows = min(G::BM, p.M - m0);
     const int nrows = min(G::BN, p.N - n0);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * p.row_bytes, mrows * p.row_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * p.row_bytes, nrows * p.row_bytes);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.a + (size_t)m0 * p.row_bytes, part_range(mrows, p.row_bytes, p.kbytes));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.b + (size_t)n0 * p.row_bytes, part_range(nrows, p.row_bytes, p.kbytes));
     const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, mrows * p.srow_bytes);
+        make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, part_range(mrows, p.srow_bytes, 4u * p.nsteps));
     const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, nrows * p.srow_bytes);
+        make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, part_range(nrows, p.srow_bytes, 4u * p.nsteps));
 
-    const int T = (int)(p.row_bytes / G::W);   // stages
+    const int T = (int)(p.kbytes / G::W);   // stages
 
     // ---- code loads: job j of this wave is 16-row block q = wave + 4j of
     // [A blocks | B blocks]; lane l holds row l/4, chunk l%4 of the block
@@ -420,6 +426,27 @@ void mx_gemm_tile(GemmArgs p)
     for (int t0 = 0; t0 < T; t0 += G::P)
         static_for<G::P>([&](auto uc) { iteration(uc, t0 + decltype(uc)::value); });
     wait_vm<0>();
+
+    // split-K: the K parts of this tile are summed by the last one to finish
+    if constexpr (!GRP && !EPI) {
+        if (p.splits > 1) {
+            auto get = [&](int j) {
+                const v16f &a = acc[j / (4 * NT)][(j / 4) % NT];
+                const int v = j % 4;
+                return v4f{a[4 * v], a[4 * v + 1], a[4 * v + 2], a[4 * v + 3]};
+            };
+            auto set = [&](int j, v4f x) {
+                v16f &a = acc[j / (4 * NT)][(j / 4) % NT];
+                const int v = j % 4;
+                a[4 * v] = x[0];
+                a[4 * v + 1] = x[1];
+                a[4 * v + 2] = x[2];
+                a[4 * v + 3] = x[3];
+            };
+            if (!splitk_reduce<4 * MT * NT, 256>(p, (int)blockIdx.x, (int)threadIdx.x, get, set))
+                return;
+        }
+    }
 
     if constexpr (OUT == OUT_F32) {
         // FP32 output (the unrounded accumulator): direct stores

@@ -37,8 +37,9 @@ struct Variant {
     int bm, bn;              // workgroup output tile
     int threads;
     KernelFn fn[2][3];       // [fmt][out]
-    int kmax[2];             // largest K per format (0: any K)
+    int kmax[2];             // largest K per format (0: any K); with split-K, of one K part
     int linear;              // 1: one-dimensional grid, the kernel maps blocks to tiles
+    int split;               // 1: the kernel takes split-K across workgroups (mx_splitk.hpp)
 };
 
 // Ring depth of the register-streaming kernel (groups in flight per wave)
@@ -54,7 +55,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
     {MXG_SFN(F, MT, WN, KW, OUT_BF16), MXG_SFN(F, MT, WN, KW, OUT_F16), MXG_SFN(F, MT, WN, KW, OUT_F32)}
 #define MXG_STREAM(MT, WN, KW)                                                        \
     {"stream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                        \
-     {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}}
+     {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0, 1}
 
 // Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
 // (K up to K8 / K4 for FP8 / FP4), NW groups of 16 B rows, each streamed by
@@ -67,7 +68,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 #define MXG_DECODE(NAME, MT, NW, G, KS, K4, K8, DMA)                                           \
     {NAME, 16 * (MT), 16 * (NW), 64 * (NW) * (KS),                                             \
      {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS, DMA), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS, DMA)},   \
-     {K8, K4}, 0}
+     {K8, K4}, 0, 0}
 
 // Decode-width tiles on the 32x32x64 instruction: waves split K, each
 // streams its run through a private register ring and LDS slot.
@@ -76,7 +77,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
     {MXG_KFN(F, MT, NT, KW, G, OUT_BF16), MXG_KFN(F, MT, NT, KW, G, OUT_F16), MXG_KFN(F, MT, NT, KW, G, OUT_F32)}
 #define MXG_SKINNY(NAME, MT, NT, KW, G)                                             \
     {NAME, 32 * (MT), 32 * (NT), 64 * (KW),                                         \
-     {MXG_KOUTS(FMT_FP8, MT, NT, KW, G), MXG_KOUTS(FMT_FP4, MT, NT, KW, G)}, {0, 0}, 0}
+     {MXG_KOUTS(FMT_FP8, MT, NT, KW, G), MXG_KOUTS(FMT_FP4, MT, NT, KW, G)}, {0, 0}, 0, 0}
 
 // Large tiles on the 32x32x64 instruction, staged through registers.
 #define MXG_TFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O>)
@@ -84,7 +85,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
     {MXG_TFN(F, MT, NT, OUT_BF16), MXG_TFN(F, MT, NT, OUT_F16), MXG_TFN(F, MT, NT, OUT_F32)}
 #define MXG_TILE(NAME, MT, NT)                                                      \
     {NAME, 64 * (MT), 64 * (NT), 256,                                               \
-     {MXG_TOUTS(FMT_FP8, MT, NT), MXG_TOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1}
+     {MXG_TOUTS(FMT_FP8, MT, NT), MXG_TOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1, 1}
 
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
@@ -118,13 +119,13 @@ constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
     {MXG_GSFN(F, MT, WN, KW, OUT_BF16), MXG_GSFN(F, MT, WN, KW, OUT_F16), MXG_GSFN(F, MT, WN, KW, OUT_F32)}
 #define MXG_GSTREAM(MT, WN, KW)                                                       \
     {"gstream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                       \
-     {MXG_GSOUTS(FMT_FP8, MT, WN, KW), MXG_GSOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0}
+     {MXG_GSOUTS(FMT_FP8, MT, WN, KW), MXG_GSOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0, 0}
 #define MXG_GTFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O, 1>)
 #define MXG_GTOUTS(F, MT, NT) \
     {MXG_GTFN(F, MT, NT, OUT_BF16), MXG_GTFN(F, MT, NT, OUT_F16), MXG_GTFN(F, MT, NT, OUT_F32)}
 #define MXG_GTILE(NAME, MT, NT)                                                     \
     {NAME, 64 * (MT), 64 * (NT), 256,                                               \
-     {MXG_GTOUTS(FMT_FP8, MT, NT), MXG_GTOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1}
+     {MXG_GTOUTS(FMT_FP8, MT, NT), MXG_GTOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1, 0}
 
 const Variant kGroupVariants[] = {
     MXG_GSTREAM(1, 2, 4),
@@ -250,6 +251,56 @@ int find_variant(const char *name)
     return 0;
 }
 
+// ------------------------------------------------------------ split-K
+// Largest number of K parts, and the K granularity of a part (128-K steps:
+// the kernels' scale codes come four steps per 16-byte row piece).
+constexpr int kMaxSplits = 64;
+constexpr int kSplitGran = 4;
+
+inline int64_t tiles_of(const Variant &v, int64_t M, int64_t N) { return cdiv(M, v.bm) * cdiv(N, v.bn); }
+
+// Floats of one partial tile in the workspace: every thread's four-float
+// pieces (the stream kernels give each thread whole pieces even where the
+// tile has fewer groups of four columns than threads).
+inline int64_t tile_floats(const Variant &v)
+{
+    return cdiv((int64_t)v.bm * v.bn / 4, v.threads) * v.threads * 4;
+}
+
+// Workspace of `splits` K parts: a fixed region of kSplitCounters arrival
+// counters (the same for every configuration, so that one workspace serves
+// any sequence of calls) and then tiles x splits partial tiles of FP32.
+constexpr size_t kCounterBytes = (size_t)kSplitCounters * 4;
+
+inline size_t splitk_bytes(const Variant &v, int splits, int64_t M, int64_t N)
+{
+    if (splits <= 1)
+        return 0;
+    const int64_t tiles = tiles_of(v, M, N);
+    return kCounterBytes + (size_t)(tiles * splits * tile_floats(v) * 4);
+}
+
+// The largest K part of `splits` parts: whole units of kSplitGran steps.
+inline int64_t part_k(int64_t K, int splits)
+{
+    const int64_t units = cdiv(K / 128, kSplitGran);
+    return std::min(K, cdiv(units, splits) * kSplitGran * 128);
+}
+
+// Whether variant v can run K in `splits` parts (every part non-empty and
+// within the variant's K limit).
+int check_split(const Variant &v, int is_fp4, int64_t M, int64_t N, int64_t K, int splits)
+{
+    if (splits < 1 || splits > kMaxSplits)
+        return MXG_ERR_CONFIG;
+    if (splits > 1 && (!v.split || splits > cdiv(K / 128, kSplitGran) || tiles_of(v, M, N) > kSplitCounters))
+        return MXG_ERR_CONFIG;
+    const int kmax = v.kmax[is_fp4 ? 1 : 0];
+    if (kmax && part_k(K, splits) > kmax)
+        return MXG_ERR_CONFIG;
+    return MXG_OK;
+}
+
 // Default tile choice, from measured sweeps on MI355X.  Up to 64 rows of A
 // the product is a B stream: for E2M1 with 5-32 rows and wide N the
 // whole-row decode kernel (A and the scales read once per workgroup), else
@@ -310,14 +361,42 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     return find_variant("tile_128x128");
 }
 
-int launch(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
-           int64_t M, int64_t N, int64_t K, int out_dtype, int variant, hipStream_t stream)
+struct Config {
+    int variant, splits;
+};
+
+// Default configuration.  Without a workspace: pick_variant, whole K per
+// workgroup.  With one: the same, except where too few output tiles leave
+// compute units idle over a long K and split-K across workgroups measured
+// faster on MI355X (E2M1; every part count also measured slower on c2,
+// c3, c4 and the K = 4096 cells):
+//   * a tile kernel launch of at most 128 tiles with K >= 8192: two K parts
+//     (512 x 4096 x 14336: 53.0 -> 39.2 us on tile_128x128; at K = 4096 the
+//     parts' extra round trip costs more than the idle half of the chip:
+//     18.0 -> 20.2 us);
+//   * 17-32 rows of E2M1 on narrow N (the whole-row decode kernel does not
+//     apply) with K >= 12288: the 32 x 64 stream tile in four K parts
+//     (32 x 4096 x 14336: 14.5 us on stream_2x1_k4 -> 12.7).
+Config pick_config(int is_fp4, int64_t M, int64_t N, int64_t K, bool with_ws)
 {
-    const Variant &v = kVariants[variant];
-    const int kmax = v.kmax[is_fp4 ? 1 : 0];
-    if (kmax && K > kmax)
-        return MXG_ERR_CONFIG;
+    Config cf{pick_variant(is_fp4, M, N, K), 1};
+    if (!with_ws)
+        return cf;
+    const Variant &v = kVariants[cf.variant];
+    const int64_t units = cdiv(K / 128, kSplitGran);
+    if (v.linear && tiles_of(v, M, N) <= 128 && K >= 8192 && units >= 2)
+        return Config{cf.variant, 2};
+    if (is_fp4 && M > 16 && M <= 32 && N < 8192 && K >= 12288 && units >= 4)
+        return Config{find_variant("stream_2x4_k8"), 4};
+    return cf;
+}
+
+// Kernel arguments of a plain product over the whole K range.
+GemmArgs make_args(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
+                   int64_t M, int64_t N, int64_t K)
+{
     GemmArgs p;
+    memset(&p, 0, sizeof(p));
     p.a = (const uint8_t *)a;
     p.b = (const uint8_t *)b;
     p.sa = (const uint8_t *)sa;
@@ -328,8 +407,17 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
     p.nsteps = (int)(K / 128);
     p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
     p.srow_bytes = (unsigned)(K / 32);
-    p.offs = nullptr;
-    p.groups = 0;
+    p.kbytes = p.row_bytes;
+    p.splits = 1;
+    return p;
+}
+
+int launch(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
+           int64_t M, int64_t N, int64_t K, int out_dtype, int variant, int splits, void *ws,
+           hipStream_t stream)
+{
+    const Variant &v = kVariants[variant];
+    GemmArgs p = make_args(is_fp4, a, b, sa, sb, c, M, N, K);
     const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
     dim3 grid;
     if (v.linear) {
@@ -340,6 +428,12 @@ int launch(int is_fp4, const void *a, const void *b, const void *sa, const void 
         if (gx > INT32_MAX || gy > 65535)
             return MXG_ERR_SHAPE;
         grid = dim3((unsigned)gx, (unsigned)gy);
+    }
+    if (splits > 1) {
+        p.splits = splits;
+        p.flags = (unsigned *)ws;
+        p.ws = (float *)((char *)ws + kCounterBytes);
+        grid.z = (unsigned)splits;
     }
     KernelFn fn = v.fn[is_fp4 ? 1 : 0][out_dtype];
     hipLaunchKernelGGL(fn, grid, dim3(v.threads), 0, stream, p);
@@ -412,17 +506,8 @@ int launch_grouped(int is_fp4, const void *a, const void *b, const void *sa, con
                    int out_dtype, int variant, hipStream_t stream)
 {
     const Variant &v = kGroupVariants[variant];
-    GemmArgs p;
-    p.a = (const uint8_t *)a;
-    p.b = (const uint8_t *)b;
-    p.sa = (const uint8_t *)sa;
-    p.sb = (const uint8_t *)sb;
-    p.c = c;
-    p.M = (int)M;                 // total rows; each workgroup narrows it to its group
-    p.N = (int)N;
-    p.nsteps = (int)(K / 128);
-    p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
-    p.srow_bytes = (unsigned)(K / 32);
+    // M: total rows; each workgroup narrows it to its group
+    GemmArgs p = make_args(is_fp4, a, b, sa, sb, c, M, N, K);
     p.offs = offs;
     p.groups = (int)groups;
     // worst case over all splits of M rows into the groups
@@ -540,19 +625,7 @@ int run_fused(int is_fp4, const void *a, const void *b, const void *sa, const vo
     rc = check_device();
     if (rc)
         return rc;
-    GemmArgs p;
-    p.a = (const uint8_t *)a;
-    p.b = (const uint8_t *)b;
-    p.sa = (const uint8_t *)sa;
-    p.sb = (const uint8_t *)sb;
-    p.c = c;
-    p.M = (int)M;
-    p.N = (int)N;
-    p.nsteps = (int)(K / 128);
-    p.row_bytes = (unsigned)(is_fp4 ? K / 2 : K);
-    p.srow_bytes = (unsigned)(K / 32);
-    p.offs = nullptr;
-    p.groups = 0;
+    GemmArgs p = make_args(is_fp4, a, b, sa, sb, c, M, N, K);
     p.bias = (const uint16_t *)bias;
     p.act = act;
     p.c_scale = (uint8_t *)c_scale;
@@ -622,17 +695,32 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
 // An empty kernel (measurement support: the launch cost alone).
 __global__ __launch_bounds__(1024) void mx_empty_kernel() {}
 
+int validate_ws(const void *ws, size_t ws_bytes)
+{
+    if (ws && ((uintptr_t)ws & 15u))
+        return MXG_ERR_PTR_ALIGN;
+    (void)ws_bytes;
+    return MXG_OK;
+}
+
 int run_default(int is_fp4, const void *a, const void *b, const void *sa, const void *sb, void *c,
-                int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream)
+                int64_t M, int64_t N, int64_t K, int out_dtype, void *ws, size_t ws_bytes,
+                hipStream_t stream)
 {
     int rc = validate(a, b, sa, sb, c, M, N, K, out_dtype);
     if (rc)
         return rc;
+    rc = validate_ws(ws, ws_bytes);
+    if (rc)
+        return rc;
+    Config cf = pick_config(is_fp4, M, N, K, true);
+    // a missing or short workspace: the whole-K configuration (correct, maybe slower)
+    if (cf.splits > 1 && (!ws || ws_bytes < splitk_bytes(kVariants[cf.variant], cf.splits, M, N)))
+        cf = pick_config(is_fp4, M, N, K, false);
     rc = check_device();
     if (rc)
         return rc;
-    return launch(is_fp4, a, b, sa, sb, c, M, N, K, out_dtype, pick_variant(is_fp4, M, N, K),
-                  stream);
+    return launch(is_fp4, a, b, sa, sb, c, M, N, K, out_dtype, cf.variant, cf.splits, ws, stream);
 }
 
 }  // namespace
@@ -640,48 +728,92 @@ int run_default(int is_fp4, const void *a, const void *b, const void *sa, const 
 extern "C" {
 
 int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream)
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
+                     size_t workspace_bytes, mxg_stream_t stream)
 {
-    return run_default(1, a, b, a_scale, b_scale, c, M, N, K, out_dtype, (hipStream_t)stream);
+    return run_default(1, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, workspace_bytes,
+                       (hipStream_t)stream);
 }
 
 int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream)
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
+                     size_t workspace_bytes, mxg_stream_t stream)
 {
-    return run_default(0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, (hipStream_t)stream);
+    return run_default(0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, workspace_bytes,
+                       (hipStream_t)stream);
 }
 
-int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
+static int check_shape(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX || K > kMaxK)
         return MXG_ERR_SHAPE;
     if (K % 128)
         return MXG_ERR_K_ALIGN;
-    return pick_variant(is_fp4 ? 1 : 0, M, N, K);
+    return MXG_OK;
+}
+
+int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, int with_workspace, int *splits)
+{
+    const int rc = check_shape(M, N, K);
+    if (rc)
+        return rc;
+    const Config cf = pick_config(is_fp4 ? 1 : 0, M, N, K, with_workspace != 0);
+    if (splits)
+        *splits = cf.splits;
+    return cf.variant;
+}
+
+int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
+{
+    return mx_default_config(is_fp4, M, N, K, 1, nullptr);
+}
+
+size_t mx_scaled_mm_workspace_bytes(int is_fp4, int64_t M, int64_t N, int64_t K)
+{
+    if (check_shape(M, N, K))
+        return 0;
+    const Config cf = pick_config(is_fp4 ? 1 : 0, M, N, K, true);
+    return splitk_bytes(kVariants[cf.variant], cf.splits, M, N);
+}
+
+size_t mx_config_workspace_bytes(int variant, int splits, int64_t M, int64_t N)
+{
+    if (variant < 0 || variant >= kNumVariants || splits < 1 || splits > kMaxSplits || M < 1 || N < 1 ||
+        M > INT32_MAX || N > INT32_MAX ||
+        (splits > 1 && (!kVariants[variant].split || tiles_of(kVariants[variant], M, N) > kSplitCounters)))
+        return 0;
+    return splitk_bytes(kVariants[variant], splits, M, N);
 }
 
 int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
-                        int out_dtype, int variant, mxg_stream_t stream)
+                        int out_dtype, int variant, int splits, void *workspace,
+                        size_t workspace_bytes, mxg_stream_t stream)
 {
     int rc = validate(a, b, a_scale, b_scale, c, M, N, K, out_dtype);
     if (rc)
         return rc;
     if (variant < 0 || variant >= kNumVariants)
         return MXG_ERR_CONFIG;
-    const int kmax = kVariants[variant].kmax[is_fp4 ? 1 : 0];
-    if (kmax && K > kmax)
-        return MXG_ERR_CONFIG;
+    rc = check_split(kVariants[variant], is_fp4, M, N, K, splits);
+    if (rc)
+        return rc;
+    rc = validate_ws(workspace, workspace_bytes);
+    if (rc)
+        return rc;
+    if (splits > 1 && (!workspace || workspace_bytes < splitk_bytes(kVariants[variant], splits, M, N)))
+        return MXG_ERR_WORKSPACE;
     rc = check_device();
     if (rc)
         return rc;
-    return launch(is_fp4 ? 1 : 0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, variant,
-                  (hipStream_t)stream);
+    return launch(is_fp4 ? 1 : 0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, variant, splits,
+                  workspace, (hipStream_t)stream);
 }
 
 int mx_empty_like(int is_fp4, int64_t M, int64_t N, int64_t K, mxg_stream_t stream)
 {
-    const int variant = mx_default_variant(is_fp4, M, N, K);
+    int splits = 1;
+    const int variant = mx_default_config(is_fp4, M, N, K, 1, &splits);
     if (variant < 0)
         return variant;
     int rc = check_device();
@@ -691,7 +823,8 @@ int mx_empty_like(int is_fp4, int64_t M, int64_t N, int64_t K, mxg_stream_t stre
     const int64_t gx = cdiv(N, v.bn), gy = cdiv(M, v.bm);
     if (v.linear ? gx * gy > INT32_MAX : (gx > INT32_MAX || gy > 65535))
         return MXG_ERR_SHAPE;
-    const dim3 grid = v.linear ? dim3((unsigned)(gx * gy)) : dim3((unsigned)gx, (unsigned)gy);
+    dim3 grid = v.linear ? dim3((unsigned)(gx * gy)) : dim3((unsigned)gx, (unsigned)gy);
+    grid.z = (unsigned)splits;
     hipLaunchKernelGGL(mx_empty_kernel, grid, dim3(v.threads), 0, (hipStream_t)stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
@@ -729,7 +862,8 @@ const char *mx_status_string(int status)
     case MXG_ERR_DTYPE: return "unknown output dtype";
     case MXG_ERR_DEVICE: return "current device is not gfx950";
     case MXG_ERR_HIP: return "HIP runtime error";
-    case MXG_ERR_CONFIG: return "invalid kernel variant";
+    case MXG_ERR_CONFIG: return "invalid kernel variant or K-part count";
+    case MXG_ERR_WORKSPACE: return "workspace missing or too small for the requested K parts";
     default: return "unknown status";
     }
 }

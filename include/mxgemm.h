@@ -75,9 +75,10 @@ typedef enum {
     MXG_ERR_K_ALIGN = -3,   /* K is not a multiple of 128 */
     MXG_ERR_PTR_ALIGN = -4, /* a, b or c is not 16-byte aligned; a scale pointer not 4-byte aligned */
     MXG_ERR_DTYPE = -5,     /* out_dtype is not an mxg_out_t */
+    MXG_ERR_WORKSPACE = -6, /* an explicit split-K configuration lacks a large enough workspace */
     MXG_ERR_DEVICE = -7,    /* the current device is not gfx950 */
     MXG_ERR_HIP = -8,       /* a HIP call failed (see mx_last_hip_error) */
-    MXG_ERR_CONFIG = -9     /* an explicit kernel variant is invalid */
+    MXG_ERR_CONFIG = -9     /* an explicit kernel variant or K-part count is invalid */
 } mxg_status_t;
 
 /*
@@ -89,35 +90,68 @@ typedef enum {
  * c            [M][N] output of type out_dtype, 16-byte aligned.
  * M, N, K      logical sizes (K counts elements, not bytes); M, N >= 1,
  *              K a positive multiple of 128 and at most 2^22.
- * out_dtype    an mxg_out_t.
+ * out_dtype    an mxg_out_t (BF16, FP16 or FP32).
+ * workspace    optional device memory for split-K across workgroups (the
+ *              small-M shapes whose output tiles are too few to occupy
+ *              every compute unit -- the pages' largest MXFP4 gain is such
+ *              a decode shape, 32 x 14336 x 4096: "PyTorch 接上 FlyDSL",
+ *              5ulink.com, section "内核级成绩"): the workgroups of one
+ *              output tile each take a part of K, write FP32 partial tiles
+ *              here, and the last to finish sums them in part order (so the
+ *              result does not depend on timing).  Needs
+ *              mx_scaled_mm_workspace_bytes(...) bytes, 16-byte aligned;
+ *              its first 64 KiB (the arrival counters, at the same place
+ *              for every shape and configuration) zero-filled once by the
+ *              caller when it is allocated.  Every call leaves them at zero
+ *              again, so one workspace serves any sequence of calls on one
+ *              stream.  NULL, or fewer bytes than needed: the product runs
+ *              without split-K -- same contract, possibly slower -- and the
+ *              workspace is not touched.  Calls that may run at the same
+ *              time (other streams) need distinct workspaces; the library
+ *              keeps no pointer to it after the call's kernels complete.
+ * workspace_bytes  size of workspace in bytes.
  * stream       HIP stream the work is enqueued on (0 = null stream).
  *
  * Returns MXG_OK after enqueueing, or an error status with nothing
- * enqueued.  No workspace is needed: the kernels never communicate between
- * workgroups.
+ * enqueued (MXG_ERR_PTR_ALIGN also for a workspace not 16-byte aligned).
  */
 int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
-                     mxg_stream_t stream);
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
+                     size_t workspace_bytes, mxg_stream_t stream);
 
 /* MXFP8 (E4M3) x MXFP8 NT scaled GEMM.  Same contract as mx_scaled_mm_fp4
  * except that a and b hold one E4M3 code per byte: [M][K] and [N][K]. */
 int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
-                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
-                     mxg_stream_t stream);
+                     void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
+                     size_t workspace_bytes, mxg_stream_t stream);
 
-/* Explicit kernel variant, for tests and tuning: run variant `variant`
- * (0 .. mx_num_variants()-1) instead of the one the default entry points
- * pick.  is_fp4: 1 for MXFP4 operands, 0 for MXFP8.  Same operand contract
- * and errors as mx_scaled_mm_fp4/fp8, plus MXG_ERR_CONFIG for an unknown
- * variant or a K beyond the variant's limit (mx_variant_max_k).  Every variant computes the same product; they differ in tiling
- * and therefore in FP32 accumulation order. */
+/* Workspace bytes mx_scaled_mm_fp4 (is_fp4 = 1) / mx_scaled_mm_fp8 (0)
+ * use for this shape: 0 when the shape runs without split-K, or is
+ * invalid.  A pure function of its arguments. */
+size_t mx_scaled_mm_workspace_bytes(int is_fp4, int64_t M, int64_t N, int64_t K);
+
+/* Explicit kernel variant and K-part count, for tests and tuning: run
+ * variant `variant` (0 .. mx_num_variants()-1) with K cut into `splits`
+ * parts (1: no split-K) instead of the default configuration.  is_fp4: 1
+ * for MXFP4 operands, 0 for MXFP8.  Same operand contract and errors as
+ * mx_scaled_mm_fp4/fp8, plus MXG_ERR_CONFIG for an unknown variant, a
+ * variant without split-K asked for splits > 1, splits outside 1 .. 64 or
+ * above K/512 (every part gets at least 512 K), or a K part beyond the
+ * variant's limit (mx_variant_max_k); MXG_ERR_WORKSPACE when splits > 1
+ * and the workspace is NULL or smaller than mx_config_workspace_bytes.
+ * Every configuration computes the same product; they differ in tiling and
+ * therefore in FP32 accumulation order. */
 int mx_scaled_mm_config(int is_fp4, const void *a, const void *b, const void *a_scale,
                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K,
-                        int out_dtype, int variant, mxg_stream_t stream);
+                        int out_dtype, int variant, int splits, void *workspace,
+                        size_t workspace_bytes, mxg_stream_t stream);
+/* Workspace bytes of an explicit configuration: 0 for splits == 1, for a
+ * variant without split-K, or for invalid arguments. */
+size_t mx_config_workspace_bytes(int variant, int splits, int64_t M, int64_t N);
 int mx_num_variants(void);
-/* Largest K a variant accepts for the format (is_fp4: 1 MXFP4, 0 MXFP8);
- * some variants keep the whole A tile in LDS and so bound K.  Returns
+/* Largest K a variant accepts for the format (is_fp4: 1 MXFP4, 0 MXFP8),
+ * per K part under split-K; some variants keep the whole A tile of their
+ * K range in LDS and so bound it.  Returns
  * MXG_ERR_CONFIG for an unknown variant.  A call with a larger K returns
  * MXG_ERR_CONFIG. */
 int64_t mx_variant_max_k(int variant, int is_fp4);
@@ -264,8 +298,12 @@ int64_t mx_fused_variant_max_k(int variant, int is_fp4);
 int mx_dense_gemm(int dtype, int trans_a, int trans_b, const void *a, const void *b, void *c,
                   int64_t M, int64_t N, int64_t K, int out_dtype, mxg_stream_t stream);
 
-/* The variant the default entry points pick for a shape (>= 0), or a
- * negative status for an invalid shape. */
+/* The configuration the default entry points pick for a shape: returns the
+ * variant (>= 0) and stores the K-part count in *splits (if not NULL), for
+ * a call given a large enough workspace (with_workspace = 1) or none (0);
+ * or a negative status for an invalid shape. */
+int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, int with_workspace, int *splits);
+/* mx_default_config(is_fp4, M, N, K, 1, NULL). */
 int mx_default_variant(int is_fp4, int64_t M, int64_t N, int64_t K);
 
 /* Measurement support: enqueue an empty kernel on exactly the grid and
@@ -285,7 +323,7 @@ int mx_last_hip_error(void);
 
 /* ABI version of this header (bumped on incompatible changes). */
 int mx_abi_version(void);
-#define MXGEMM_ABI_VERSION 7
+#define MXGEMM_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -27,10 +27,15 @@ def lib():
         spec.loader.exec_module(mod)
         mod.build()
     L = ctypes.CDLL(LIB)
-    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    L.mx_scaled_mm_fp4.argtypes = [P, P, P, P, P, I64, I64, I64, INT, P]
+    P, I64, INT, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.mx_scaled_mm_fp4.argtypes = [P, P, P, P, P, I64, I64, I64, INT, P, SZ, P]
     L.mx_scaled_mm_fp8.argtypes = L.mx_scaled_mm_fp4.argtypes
-    L.mx_scaled_mm_config.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, INT, P]
+    L.mx_scaled_mm_config.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, INT, INT, P, SZ, P]
+    L.mx_scaled_mm_workspace_bytes.argtypes = [INT, I64, I64, I64]
+    L.mx_scaled_mm_workspace_bytes.restype = SZ
+    L.mx_config_workspace_bytes.argtypes = [INT, INT, I64, I64]
+    L.mx_config_workspace_bytes.restype = SZ
+    L.mx_default_config.argtypes = [INT, I64, I64, I64, INT, ctypes.POINTER(INT)]
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_variant_name.restype = ctypes.c_char_p
     L.mx_default_variant.argtypes = [INT, I64, I64, I64]
@@ -63,7 +68,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 7
+    assert lib.mx_abi_version() == 8
     assert lib.mx_num_variants() >= 1
     for v in range(lib.mx_num_variants()):
         assert lib.mx_variant_name(v)
@@ -102,7 +107,7 @@ A = 0x10000   # fake but aligned device addresses: validation never dereferences
     ((A, A, A, A, A, 8, 8, (1 << 22) + 128, 0), -2),  # K beyond the per-workgroup buffer range
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(lib, fn, args, status):
-    rc = getattr(lib, fn)(*args, None)
+    rc = getattr(lib, fn)(*args, None, 0, None)
     assert rc == status, (rc, lib.mx_status_string(rc))
 
 
@@ -222,8 +227,8 @@ def test_dense_invalid_arguments(lib, args, status):
 
 def test_invalid_configs(lib):
     ok = (A, A, A, A, A, 64, 64, 512, 0)
-    assert lib.mx_scaled_mm_config(1, *ok, -1, None) == -9
-    assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, -1, 1, None, 0, None) == -9
+    assert lib.mx_scaled_mm_config(1, *ok, lib.mx_num_variants(), 1, None, 0, None) == -9
     # a variant that keeps A resident in LDS rejects K beyond its capacity
     for v in range(lib.mx_num_variants()):
         for is4 in (0, 1):
@@ -231,16 +236,78 @@ def test_invalid_configs(lib):
             assert kmax >= 512 and kmax % 128 == 0
             if kmax < (1 << 22):
                 args = (A, A, A, A, A, 64, 64, kmax + 128, 0)
-                assert lib.mx_scaled_mm_config(is4, *args, v, None) == -9
+                assert lib.mx_scaled_mm_config(is4, *args, v, 1, None, 0, None) == -9
     assert lib.mx_variant_max_k(-1, 1) == -9
     assert lib.mx_variant_max_k(lib.mx_num_variants(), 0) == -9
     # argument errors take precedence over the variant check
-    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 64, 64, 500, 0, 0, None) == -3
-    assert lib.mx_scaled_mm_config(0, 0, A, A, A, A, 64, 64, 512, 0, 0, None) == -1
+    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 64, 64, 500, 0, 0, 1, None, 0, None) == -3
+    assert lib.mx_scaled_mm_config(0, 0, A, A, A, A, 64, 64, 512, 0, 0, 1, None, 0, None) == -1
+
+
+def _variant(lib, name):
+    return next(v for v in range(lib.mx_num_variants()) if lib.mx_variant_name(v).decode() == name)
+
+
+def test_split_k_configs(lib):
+    """Split-K across workgroups: K-part counts, workspace size and errors,
+    all decided on the host before any HIP call."""
+    tile = _variant(lib, "tile_128x128")
+    skinny = _variant(lib, "skinny_64x64_k4")
+    M, N, K = 512, 4096, 4096
+    args = (A, A, A, A, A, M, N, K, 0)
+    # workspace: the fixed region of 16384 counters, then 128 x 2 partial
+    # tiles of 128 x 128 FP32
+    need = lib.mx_config_workspace_bytes(tile, 2, M, N)
+    assert need == 16384 * 4 + 128 * 2 * 128 * 128 * 4
+    # split-K only on launches of at most 16384 tiles
+    assert lib.mx_config_workspace_bytes(tile, 2, 128 * 128, 128 * 129) == 0
+    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 128 * 128, 128 * 129, K, 0, tile, 2, A, 1 << 40, None) == -9
+    assert lib.mx_config_workspace_bytes(tile, 1, M, N) == 0
+    assert lib.mx_config_workspace_bytes(tile, 0, M, N) == 0
+    assert lib.mx_config_workspace_bytes(-1, 2, M, N) == 0
+    # splits > 1 needs a large enough workspace
+    assert lib.mx_scaled_mm_config(1, *args, tile, 2, None, 0, None) == -6
+    assert lib.mx_scaled_mm_config(1, *args, tile, 2, A, need - 1, None) == -6
+    # ... 16-byte aligned
+    assert lib.mx_scaled_mm_config(1, *args, tile, 2, A + 8, need, None) == -4
+    # part counts out of range: at least 512 K per part, at most 64 parts
+    assert lib.mx_scaled_mm_config(1, *args, tile, 0, A, need, None) == -9
+    assert lib.mx_scaled_mm_config(1, *args, tile, 9, A, 1 << 40, None) == -9      # 4096 / 512 = 8
+    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, M, N, 1 << 16, 0, tile, 65, A, 1 << 40, None) == -9
+    # a kernel without split-K rejects splits > 1
+    assert lib.mx_scaled_mm_config(1, *args, skinny, 2, A, 1 << 40, None) == -9
+    # the decode kernels (A tile of the whole K in LDS) take no split-K
+    dec = _variant(lib, "decode_32x64")
+    assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 32, 14336, 4096, 0, dec, 2, A, 1 << 40, None) == -9
+    assert lib.mx_config_workspace_bytes(dec, 2, 32, 14336) == 0
+    assert lib.mx_scaled_mm_fp4(*args, A + 4, 1 << 30, None) == -4
+    # (valid configurations, which get as far as the device check, are
+    # exercised by tests/sanitize/abi_driver.c against a build without
+    # device code, so that no kernel can ever start on fake pointers)
+
+
+def test_default_config(lib):
+    sp = ctypes.c_int(0)
+    for shape in ((1, 4096, 4096), (32, 14336, 4096), (64, 4096, 4096), (512, 4096, 4096),
+                  (256, 28672, 8192), (8192, 8192, 8192)):
+        for is4 in (0, 1):
+            for with_ws in (0, 1):
+                v = lib.mx_default_config(is4, *shape, with_ws, ctypes.byref(sp))
+                assert 0 <= v < lib.mx_num_variants()
+                assert 1 <= sp.value <= 64
+                if not with_ws:
+                    assert sp.value == 1
+            v = lib.mx_default_config(is4, *shape, 1, ctypes.byref(sp))
+            need = lib.mx_scaled_mm_workspace_bytes(is4, *shape)
+            assert need == lib.mx_config_workspace_bytes(v, sp.value, shape[0], shape[1])
+            assert (need > 0) == (sp.value > 1)
+            assert lib.mx_default_variant(is4, *shape) == v
+    assert lib.mx_default_config(1, 8, 8, 100, 1, None) == -3
+    assert lib.mx_scaled_mm_workspace_bytes(1, 8, 8, 100) == 0
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, -7, -8, -9):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.mx_status_string(s) != b"unknown status"
     assert b"128" in lib.mx_status_string(-3)
     assert lib.mx_status_string(-1234) == b"unknown status"
@@ -294,6 +361,34 @@ DEFAULTS = [
 def test_default_variant_choice(lib, is4, M, N, K, name):
     lib.mx_variant_max_k.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.mx_variant_max_k.restype = ctypes.c_int64
-    v = lib.mx_default_variant(is4, M, N, K)
+    # without a workspace (with one, split-K may take over: see SPLIT_DEFAULTS)
+    sp = ctypes.c_int(0)
+    v = lib.mx_default_config(is4, M, N, K, 0, ctypes.byref(sp))
     assert lib.mx_variant_name(v).decode() == name
+    assert sp.value == 1
     assert K <= lib.mx_variant_max_k(v, is4)
+
+
+# With a workspace: split-K across workgroups where it measured faster on
+# MI355X (few output tiles over a long K), the whole-K choice elsewhere.
+SPLIT_DEFAULTS = [
+    # (is_fp4, M, N, K, variant, K parts)
+    (1, 512, 4096, 14336, "tile_128x128", 2),
+    (1, 512, 4096, 4096, "tile_128x128", 1),
+    (1, 32, 4096, 14336, "stream_2x4_k8", 4),
+    (1, 32, 4096, 4096, "stream_2x1_k4", 1),
+    (1, 32, 14336, 4096, "decode_32x64", 1),
+    (0, 64, 4096, 4096, "stream_2x2_k4", 1),
+    (1, 256, 28672, 8192, "tile_128x256", 1),
+    (1, 8192, 8192, 8192, "tile_256x256", 1),
+    (1, 2048, 4096, 14336, "tile_128x256", 1),
+]
+
+
+@pytest.mark.parametrize("is4,M,N,K,name,parts", SPLIT_DEFAULTS, ids=lambda x: str(x))
+def test_default_config_with_workspace(lib, is4, M, N, K, name, parts):
+    sp = ctypes.c_int(0)
+    v = lib.mx_default_config(is4, M, N, K, 1, ctypes.byref(sp))
+    assert lib.mx_variant_name(v).decode() == name
+    assert sp.value == parts
+    assert (lib.mx_scaled_mm_workspace_bytes(is4, M, N, K) > 0) == (parts > 1)

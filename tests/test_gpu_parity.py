@@ -34,16 +34,17 @@ def dev(x):
 
 
 def run(mx, fmt, a, b, sa, sb, M, N, K, out="f32", variant=None, stream=None,
-        inputs_on_device=False):
+        inputs_on_device=False, splits=1, workspace="auto"):
     """One call through the C ABI; returns float64 (f32) or uint16 bits (bf16/f16)."""
     da, db, dsa, dsb = (a, b, sa, sb) if inputs_on_device else (dev(a), dev(b), dev(sa), dev(sb))
     c = torch.empty((M, N), dtype=OUT[out], device="cuda")
     is_fp4 = fmt == "fp4"
     if variant is None:
         fn = mx.mx_scaled_mm_fp4 if is_fp4 else mx.mx_scaled_mm_fp8
-        fn(da, db, dsa, dsb, c, M, N, K, stream=stream)
+        fn(da, db, dsa, dsb, c, M, N, K, workspace=workspace, stream=stream)
     else:
-        mx.mx_scaled_mm_config(is_fp4, da, db, dsa, dsb, c, M, N, K, variant, stream=stream)
+        mx.mx_scaled_mm_config(is_fp4, da, db, dsa, dsb, c, M, N, K, variant, splits=splits,
+                               workspace=workspace, stream=stream)
     if stream is not None:
         stream.synchronize()
     torch.cuda.synchronize()
@@ -66,16 +67,16 @@ def e4m3_model(fmt, a, b, sa, sb, M, N, K):
     return mxcheck.E4M3RunModel(a, b, sa, sb, M, N, K) if fmt == "fp8" else None
 
 
-def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, what=""):
+def full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=None, what="", splits=1, workspace="auto"):
     cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
     model = e4m3_model(fmt, a, b, sa, sb, M, N, K)
-    c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", variant)
+    c32 = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", variant, splits=splits, workspace=workspace)
     _, n_model = mxcheck.check_f32(c32, cref, S, K, model, what)
     if n_model:
         print("  %s: %d of %d elements within the bound of the E4M3 instruction's value only"
               % (what, n_model, c32.size), flush=True)
     for kind in ("bf16", "f16"):
-        bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, variant)
+        bits = run(mx, fmt, a, b, sa, sb, M, N, K, kind, variant, splits=splits, workspace=workspace)
         mxcheck.check_rounded(bits, cref, S, K, kind, model, what + " " + kind)
         # the epilogue is exactly round-to-nearest-even of the FP32 accumulator
         rne = oracle.round_bf16(c32) if kind == "bf16" else oracle.round_f16(c32)
@@ -360,3 +361,67 @@ def test_every_variant_long_k(mx, fmt):
         print("long K", fmt, mx.mx_variant_name(v), K, flush=True)
         full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v,
                    what="%s %s K=%d" % (fmt, mx.mx_variant_name(v), K))
+
+
+
+# ----------------------------------------------------------------- split-K
+def split_variants(mx, fmt, M, N, K):
+    """Variants that take split-K and accept a K part of this shape."""
+    out = []
+    for v in range(mx.mx_num_variants()):
+        if mx.mx_config_workspace_bytes(v, 2, M, N) == 0:
+            continue
+        if (K // 2 + 511) // 512 * 512 <= mx.mx_variant_max_k(v, fmt == "fp4"):
+            out.append(v)
+    return out
+
+
+# K/512 = 5 parts' worth of whole groups (ragged split), 2.25 (a tail of one
+# step in the last part), 8; M and N ragged against every tile
+SPLIT_SHAPES = [(70, 200, 2560), (33, 100, 1152), (130, 90, 4096)]
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_split_k_every_variant(mx, fmt, shape):
+    M, N, K = shape
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=M * 17 + N + K)
+    units = (K // 128 + 3) // 4
+    for v in split_variants(mx, fmt, M, N, K):
+        for splits in sorted({2, 3, units}):
+            if splits > units:
+                continue
+            what = "%s %s %s splits=%d" % (fmt, shape, mx.mx_variant_name(v), splits)
+            print("split-K", what, flush=True)
+            full_check(mx, fmt, a, b, sa, sb, M, N, K, variant=v, what=what, splits=splits)
+
+
+def test_split_k_deterministic_and_workspace_reused(mx):
+    # the same workspace across calls: its counters are back at zero after
+    # each call, and the fixed part order gives identical bits every time
+    fmt, M, N, K = "fp4", 100, 300, 4096
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=31)
+    cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+    ops = (dev(a), dev(b), dev(sa), dev(sb))
+    for v in split_variants(mx, fmt, M, N, K):
+        ws = torch.zeros(mx.mx_config_workspace_bytes(v, 4, M, N), dtype=torch.uint8, device="cuda")
+        outs = []
+        for _ in range(3):
+            c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            mx.mx_scaled_mm_config(True, *ops, c, M, N, K, v, splits=4, workspace=ws)
+            outs.append(c)
+        torch.cuda.synchronize()
+        # a counter left set would leave a later call's tiles unwritten
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0]), mx.mx_variant_name(v) + ": split-K result not deterministic"
+        mxcheck.check_f32(outs[0].cpu().numpy().astype(np.float64), cref, S, K, None,
+                          "%s splits=4" % mx.mx_variant_name(v))
+
+
+@pytest.mark.parametrize("name", ["c2_fp4_32x14336x4096", "c3_fp8_64x4096x4096"])
+def test_default_without_workspace(mx, name):
+    # the default entry points with no workspace run the whole-K configuration
+    cs = _case(name)
+    cref, S = oracle.gemm(cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K)
+    c32 = run(mx, cs.fmt, cs.a, cs.b, cs.sa, cs.sb, cs.M, cs.N, cs.K, "f32", workspace=None)
+    mxcheck.check_f32(c32, cref, S, cs.K, None, name + " without workspace")
