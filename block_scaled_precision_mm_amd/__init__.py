@@ -53,6 +53,8 @@ _lib.mx_config_workspace_bytes.argtypes = [_INT, _INT, _I64, _I64]
 _lib.mx_config_workspace_bytes.restype = _SZ
 _lib.mx_default_config.argtypes = [_INT, _I64, _I64, _I64, _INT, ctypes.POINTER(_INT)]
 _lib.mx_default_variant.argtypes = [_INT, _I64, _I64, _I64]
+_lib.mx_scaled_mm_noalloc.argtypes = [_INT, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
+_lib.mx_noalloc_scratch_bytes.restype = _SZ
 _lib.mx_variant_max_k.argtypes = [_INT, _INT]
 _lib.mx_variant_max_k.restype = _I64
 _lib.mx_status_string.argtypes = [_INT]
@@ -75,7 +77,7 @@ _lib.mx_fused_variant_max_k.restype = _I64
 _lib.mx_dense_gemm.argtypes = [_INT, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]
 _lib.mx_empty_like.argtypes = [_INT, _I64, _I64, _I64, _P]
 for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
-           "mx_default_config",
+           "mx_default_config", "mx_scaled_mm_noalloc",
            "mx_last_hip_error", "mx_abi_version", "mx_default_variant", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
            "mx_grouped_num_variants", "mx_grouped_default_variant", "mx_scaled_mm_fused",
@@ -85,6 +87,7 @@ for _f in ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_nu
 # every symbol include/mxgemm.h declares
 EXPORTS = ("mx_scaled_mm_fp4", "mx_scaled_mm_fp8", "mx_scaled_mm_config", "mx_num_variants",
            "mx_scaled_mm_workspace_bytes", "mx_config_workspace_bytes", "mx_default_config",
+           "mx_scaled_mm_noalloc", "mx_noalloc_scratch_bytes",
            "mx_variant_max_k", "mx_variant_name", "mx_default_variant", "mx_status_string",
            "mx_last_hip_error", "mx_abi_version", "mx_quantize_bf16",
            "mx_grouped_mm_fp4", "mx_grouped_mm_fp8", "mx_grouped_mm_config",
@@ -414,3 +417,18 @@ def mx_empty_like(is_fp4, M, N, K, stream=None) -> None:
     st = _lib.mx_empty_like(int(bool(is_fp4)), M, N, K, _stream(stream))
     if st:
         raise MxGemmError(st, "mx_empty_like")
+
+
+def mx_scaled_mm_noalloc(is_fp4, a, b, a_scale, b_scale, c, M, N, K, out_dtype=None, stream=None) -> None:
+    """The default product with the library's built-in split-K scratch
+    (C ABI mx_scaled_mm_noalloc): no workspace argument and no allocation.
+    Calls that may overlap on one GPU race on that scratch."""
+    _check_tensors(bool(is_fp4), a, b, a_scale, b_scale, c, M, N, K)
+    st = _lib.mx_scaled_mm_noalloc(int(bool(is_fp4)), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                   _ptr(c), M, N, K, _out_code(c, out_dtype), _stream(stream))
+    if st:
+        raise MxGemmError(st, "mx_scaled_mm_noalloc")
+
+
+def mx_noalloc_scratch_bytes() -> int:
+    return int(_lib.mx_noalloc_scratch_bytes())

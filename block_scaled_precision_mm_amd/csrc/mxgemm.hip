@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/mxgemm.h"
 #include "mx_decode.hpp"
@@ -695,6 +696,60 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
 // An empty kernel (measurement support: the launch cost alone).
 __global__ __launch_bounds__(1024) void mx_empty_kernel() {}
 
+// ------------------------------------------------- allocation-free entry point
+// mx_scaled_mm_noalloc runs the default configuration with the split-K
+// workspace in this array instead of a caller's buffer.  Each GPU the
+// library runs on holds its own copy until the process ends.  Its size
+// covers every default split-K configuration (at most 64 KiB of counters
+// plus 128 tiles x 2 parts x 128 x 128 FP32 = 16.06 MiB).
+constexpr size_t kScratchBytes = (size_t)20 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's scratch, looked up once per device with the
+// device current (the array's name is not a device address on the host),
+// and its counter region cleared by a fill kernel on the first call's
+// stream, ahead of that call's own kernels.
+__global__ __launch_bounds__(256) void mx_zero_words(unsigned *p, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_of_device(hipStream_t stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXG_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return MXG_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            g_last_hip_error = (int)e;
+            return MXG_ERR_HIP;
+        }
+        hipLaunchKernelGGL(mx_zero_words, dim3(kSplitCounters / 256), dim3(256), 0, stream, (unsigned *)ptr,
+                           kSplitCounters);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return MXG_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MXG_OK;
+}
+
 int validate_ws(const void *ws, size_t ws_bytes)
 {
     if (ws && ((uintptr_t)ws & 15u))
@@ -742,6 +797,32 @@ int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const vo
     return run_default(0, a, b, a_scale, b_scale, c, M, N, K, out_dtype, workspace, workspace_bytes,
                        (hipStream_t)stream);
 }
+
+int mx_scaled_mm_noalloc(int is_fp4, const void *a, const void *b, const void *a_scale,
+                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
+                         mxg_stream_t stream)
+{
+    is_fp4 = is_fp4 ? 1 : 0;
+    int rc = validate(a, b, a_scale, b_scale, c, M, N, K, out_dtype);
+    if (rc)
+        return rc;
+    const Config cf = pick_config(is_fp4, M, N, K, true);
+    if (splitk_bytes(kVariants[cf.variant], cf.splits, M, N) > kScratchBytes)
+        return MXG_ERR_SCRATCH;
+    rc = check_device();
+    if (rc)
+        return rc;
+    void *ws = nullptr;
+    if (cf.splits > 1) {
+        rc = scratch_of_device((hipStream_t)stream, &ws);
+        if (rc)
+            return rc;
+    }
+    return launch(is_fp4, a, b, a_scale, b_scale, c, M, N, K, out_dtype, cf.variant, cf.splits, ws,
+                  (hipStream_t)stream);
+}
+
+size_t mx_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 static int check_shape(int64_t M, int64_t N, int64_t K)
 {
@@ -864,6 +945,7 @@ const char *mx_status_string(int status)
     case MXG_ERR_HIP: return "HIP runtime error";
     case MXG_ERR_CONFIG: return "invalid kernel variant or K-part count";
     case MXG_ERR_WORKSPACE: return "workspace missing or too small for the requested K parts";
+    case MXG_ERR_SCRATCH: return "the shape needs more split-K workspace than mx_scaled_mm_noalloc's built-in scratch holds";
     default: return "unknown status";
     }
 }

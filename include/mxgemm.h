@@ -78,7 +78,8 @@ typedef enum {
     MXG_ERR_WORKSPACE = -6, /* an explicit split-K configuration lacks a large enough workspace */
     MXG_ERR_DEVICE = -7,    /* the current device is not gfx950 */
     MXG_ERR_HIP = -8,       /* a HIP call failed (see mx_last_hip_error) */
-    MXG_ERR_CONFIG = -9     /* an explicit kernel variant or K-part count is invalid */
+    MXG_ERR_CONFIG = -9,    /* an explicit kernel variant or K-part count is invalid */
+    MXG_ERR_SCRATCH = -10   /* mx_scaled_mm_noalloc: the shape needs more scratch than it has */
 } mxg_status_t;
 
 /*
@@ -124,6 +125,28 @@ int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const vo
 int mx_scaled_mm_fp8(const void *a, const void *b, const void *a_scale, const void *b_scale,
                      void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,
                      size_t workspace_bytes, mxg_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as mx_scaled_mm_fp4 (is_fp4 = 1) / mx_scaled_mm_fp8 (0) with a
+ * large enough workspace, whose split-K workspace is instead a static array
+ * inside the library, one per GPU, of mx_noalloc_scratch_bytes() bytes (20
+ * MiB, held until the process ends).  The call allocates nothing: no
+ * hipMalloc or allocating library routine, here or in any call (the first
+ * call on a GPU looks up the array's address and clears its counters with
+ * a small kernel on `stream`).  The caller still provides a, b, the scales
+ * and c as for mx_scaled_mm_fp4/fp8.  All calls on one GPU share the array:
+ * calls that may overlap on one GPU (other streams, other threads) race
+ * and must be serialized by the caller.  Returns the statuses of
+ * mx_scaled_mm_fp4/fp8, plus MXG_ERR_SCRATCH, before anything is enqueued,
+ * for a shape whose default configuration needs more workspace than the
+ * array holds (none of the current ones does: at most 16.1 MiB).
+ */
+int mx_scaled_mm_noalloc(int is_fp4, const void *a, const void *b, const void *a_scale,
+                         const void *b_scale, void *c, int64_t M, int64_t N, int64_t K, int out_dtype,
+                         mxg_stream_t stream);
+size_t mx_noalloc_scratch_bytes(void);
 
 /* Workspace bytes mx_scaled_mm_fp4 (is_fp4 = 1) / mx_scaled_mm_fp8 (0)
  * use for this shape: 0 when the shape runs without split-K, or is

@@ -74,6 +74,12 @@ int main(void)
           MXG_ERR_CONFIG);
     rc = mx_empty_like(1, 32, 256, 256, NULL);
     CHECK(STOPPED(rc));
+    /* the allocation-free entry point: validation, then the device */
+    CHECK(mx_noalloc_scratch_bytes() >= mx_scaled_mm_workspace_bytes(1, 512, 4096, 14336));
+    CHECK(STOPPED(mx_scaled_mm_noalloc(1, a, a, a, a, a, 512, 4096, 14336, 0, NULL)));
+    CHECK(STOPPED(mx_scaled_mm_noalloc(0, a, a, a, a, a, 64, 4096, 4096, 2, NULL)));
+    CHECK(mx_scaled_mm_noalloc(1, a, a, a, a, NULL, 8, 8, 128, 0, NULL) == MXG_ERR_NULL);
+    CHECK(mx_scaled_mm_noalloc(1, a, a, a, a, a, 8, 8, 100, 0, NULL) == MXG_ERR_K_ALIGN);
     /* rejected calls */
     CHECK(mx_scaled_mm_config(1, a, a, a, a, a, 512, 4096, 4096, 0, tile, 2, a, need - 1, NULL) ==
           MXG_ERR_WORKSPACE);

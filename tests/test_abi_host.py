@@ -307,7 +307,7 @@ def test_default_config(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         assert lib.mx_status_string(s) != b"unknown status"
     assert b"128" in lib.mx_status_string(-3)
     assert lib.mx_status_string(-1234) == b"unknown status"
@@ -392,3 +392,18 @@ def test_default_config_with_workspace(lib, is4, M, N, K, name, parts):
     assert lib.mx_variant_name(v).decode() == name
     assert sp.value == parts
     assert (lib.mx_scaled_mm_workspace_bytes(is4, M, N, K) > 0) == (parts > 1)
+
+
+def test_noalloc_argument_checks(lib):
+    """The allocation-free entry point validates like the others, before
+    any HIP call."""
+    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mx_scaled_mm_noalloc.argtypes = [INT, P, P, P, P, P, I64, I64, I64, INT, P]
+    lib.mx_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    assert lib.mx_scaled_mm_noalloc(1, A, A, A, A, 0, 8, 8, 128, 0, None) == -1
+    assert lib.mx_scaled_mm_noalloc(0, A, A, A, A, A, 8, 8, 100, 0, None) == -3
+    assert lib.mx_scaled_mm_noalloc(1, A + 8, A, A, A, A, 8, 8, 128, 0, None) == -4
+    assert lib.mx_scaled_mm_noalloc(1, A, A, A, A, A, 8, 8, 128, 9, None) == -5
+    # its scratch holds the largest default split-K workspace
+    assert lib.mx_noalloc_scratch_bytes() >= lib.mx_scaled_mm_workspace_bytes(1, 512, 4096, 14336) > 0
+    assert b"scratch" in lib.mx_status_string(-10)
