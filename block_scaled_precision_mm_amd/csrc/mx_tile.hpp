@@ -15,39 +15,50 @@
 // The kernel passes B rows as X and A rows as Y, so lane (r, g) holds
 // C[m0 + r][n0 + 8v + 4g + e]: four runs of four consecutive columns.
 //
-// Stages.  One stage is 64 bytes of every tile row: 128 K values of E2M1
-// (two MFMA sub-steps) or 64 of E4M3 (one sub-step), so both formats share
-// the loader and the LDS layout.  In either format chunk 2h + g (16 bytes)
-// of a row's stage is what lane (r, g) needs for half h.
+// Super-stages.  The K loop advances 128 bytes of every tile row at a time:
+// 256 K values of E2M1 (four MFMA sub-steps) or 128 of E4M3 (two).  What
+// decided the width, measured on MI355X at 8192^3 E2M1 with loads alone
+// (every workgroup streaming its 256 + 256 rows from L2): 16-byte loads in
+// which 8 lanes read one row's 128 contiguous bytes move the operands at
+// 25.6 TB/s over the chip, against 15.2 TB/s when 4 lanes read 64 bytes of
+// a row (each L1 request then covers half a cache line, and the number of
+// requests in flight, not bytes, sets the rate); loads straight into LDS
+// stream as fast as loads into registers (26.5 TB/s).  What the loop waits
+// on is LDS: fragment reads run at 124 B per clock per compute unit in this
+// layout (measured), and a 128 x 128 wave tile reads 512 bytes of
+// fragments per MFMA besides the 256 bytes the loads write.
 //
-// Data path (measured on MI355X, which settled the design):
-//   * global -> registers with 16-byte loads in which every four
-//     consecutive lanes read one row's 64 bytes (as cheap per byte as a
-//     contiguous load), then registers -> LDS with 16-byte stores.  Direct
-//     global-to-LDS loads were tried first: they fix the LDS layout to the
-//     load's lane order, which makes the fragment reads bank-conflicted,
-//     and their load cost grows with every row touched;
-//   * LDS layout: rows in groups of 8, chunk-major inside a group with a
-//     padded chunk stride, so a fragment read (8 consecutive lanes = 8 rows
-//     of one chunk) and a staging store both run at full LDS rate;
-//   * scale codes: 16 bytes per row (four 128-K steps) fetched once per
-//     period of P stages and stored transposed ([step][row] dwords), so a
-//     stage's scale read is one contiguous dword per lane.
+// Data path.  Global -> LDS directly (gfx950's 16-byte buffer load to LDS:
+// no staging registers, no LDS store instructions).  A load instruction
+// fills 1 KB of LDS in lane order: 8 rows x 128 bytes, lane l at 16*l, so
+// lane l (row l/8 of its block, position p = l%8) fetches the row's chunk
+// c = p ^ s(row), s(row) = (row >> 1) & 7: the 8 lanes of a row still read
+// its 128 contiguous bytes, and chunk c of row `row` sits at
+// 128*row + 16*(c ^ s(row)).  A fragment read (16 consecutive lanes = 16
+// consecutive rows, one chunk) then touches 16 different 16-byte bank
+// groups: the rows alternate between the two 128-byte halves of the 256
+// bytes the LDS banks cover, and s() spreads the 8 rows of each half.
+// Scale codes: 16 bytes per row per period of four 128-K steps, through
+// registers, stored transposed ([step][row] dwords), so an MFMA's scale
+// operand is one dword read plus a shift; the two sub-steps of a 128-K
+// step share the dword (read once).  The two code slots and the scale
+// buffers are separate LDS objects, so the compiler can tell a fragment
+// read of one slot from the loads still landing in the other.
+//
+// Pipeline (iteration u computes super-stage u; two code slots).  Sub-step
+// h's fragments are read while sub-step h-1's MFMAs run.  Before the last
+// sub-step: wait for super-stage u+1's loads, barrier (every wave's loads
+// of u+1 have landed and every wave is done reading slot u), issue the
+// loads of u+2 into slot u, and at a period start write the next period's
+// scale codes and load the one after; the last sub-step's MFMAs then cover
+// the read of super-stage u+1's first fragments.  A load has one iteration
+// to land.  The loop runs whole periods; super-stages past K (and rows past
+// M or N) load zero codes through out-of-range offsets and have zero scale
+// codes, and add exactly +0.
 //
 // Waves.  Four waves in 2 x 2, each owning a (32*MT) x (32*NT) part of the
 // (64*MT) x (64*NT) workgroup tile; at MT = NT = 4 the 256 accumulator
 // registers per lane fill the accumulation register file.
-//
-// Pipeline (iteration t computes stage t).  Two LDS code slots and two
-// register staging sets: in iteration t the wave stores stage t+2 from its
-// staging set into the slot stage t used, reloads that set with stage t+4,
-// reads stage t+1's fragments into the idle fragment set and runs stage t's
-// MFMAs.  A load therefore has two iterations to land.  Each iteration
-// starts with one wait (everything issued two iterations ago has landed)
-// and one barrier; its body has no branch, and sched_group_barrier
-// interleaves MFMAs with the stores, loads and reads.  The loop runs whole
-// periods; stages past K (and rows past M or N) read as zero codes with zero
-// scale codes and add exactly +0.
 //
 // Epilogue.  FP32 output is stored straight from the accumulators.  16-bit
 // output is converted, staged through LDS and written as whole row segments
@@ -71,30 +82,26 @@ namespace mxg {
 template <int F, int MT, int NT>
 struct TileGeom {
     static constexpr int BM = 64 * MT, BN = 64 * NT;    // workgroup tile
-    static constexpr int W = 64;                         // row bytes per stage
     static constexpr int ROWS = BM + BN;                 // A rows then B rows
-    // code slot layout: rows in groups of 8; in a group, chunk c (16 bytes of
-    // each of the 8 rows, 128 contiguous bytes) starts at c * CHUNK; the 32
-    // bytes of padding per chunk put consecutive groups' chunks on
-    // complementary LDS bank halves (measured on MI355X: fragment reads at
-    // ~92% and stores at 100% of the contiguous rate, against 75% and 40%
-    // without padding)
-    static constexpr int CHUNK = 160, GROUP = 4 * CHUNK;
-    static constexpr int CODE = ROWS / 8 * GROUP;        // one code slot
-    static constexpr int LC = ROWS / 16 / 4;             // 16-row code loads per wave per stage
-    // scale codes: 16 bytes per row per period of P stages (4 steps of 128 K)
-    static constexpr int P = F == FMT_FP4 ? 4 : 8;
+    static constexpr int SW = 128;                       // row bytes per super-stage
+    static constexpr int SUB = F == FMT_FP4 ? 4 : 2;     // 32x32x64 sub-steps per super-stage
+    static constexpr int STEPS = F == FMT_FP4 ? 2 : 1;   // 128-K steps per super-stage
+    static constexpr int SLOT = ROWS * SW;               // one code slot (unpadded, swizzled)
+    static constexpr int LB = ROWS / 8 / 4;              // 1 KB loads per wave per super-stage
+    // scale codes: 16 bytes per row per period of 4 steps
+    static constexpr int P = 4 / STEPS;                  // super-stages per period
     static constexpr int SJOBS = cdiv_c(ROWS, 64);       // 64-row scale loads per period
     static constexpr int LS = cdiv_c(SJOBS, 4);          // per wave (jobs past SJOBS load nothing)
     static constexpr int SROWS = 64 * 4 * LS;            // scale rows incl. padding
     static constexpr int SCB = SROWS * 16;               // one scale buffer: [dword][row]
-    static constexpr int SC_OFF = 2 * CODE;
-    static constexpr int BYTES = SC_OFF + 2 * SCB;
-    static_assert((BM / 16) % 4 == 0 && (BN / 16) % 4 == 0, "code loads must spread evenly over 4 waves");
-    // byte offset of 16-byte chunk c (0..3) of tile row `row` in a code slot
+    static constexpr int BYTES = 2 * SLOT + 2 * SCB;
+    static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
+    static_assert((ROWS / 8) % 4 == 0, "load blocks must spread evenly over 4 waves");
+    static_assert(LB + LS < 64, "outstanding loads must fit the vmcnt field");
+    // byte offset of 16-byte chunk c (0..7) of tile row `row` in a code slot
     __device__ static constexpr int code_off(int row, int c)
     {
-        return (row >> 3) * GROUP + c * CHUNK + (row & 7) * 16;
+        return row * SW + 16 * (c ^ ((row >> 1) & 7));
     }
 };
 
@@ -131,42 +138,6 @@ __device__ __forceinline__ void static_for(Fn &&f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The memory operations of one iteration, in program order: at a period
-// start the scale-code writes (4 per scale load) and loads; then, per code
-// load, the LDS write that empties a staging register and the load that
-// refills it; then the fragment and scale reads.  sched_group_barrier masks:
-// 0x200 LDS write, 0x020 vector-memory read, 0x100 LDS read.
-template <bool PERIOD, int LS, int LC, int NREAD>
-struct OpSeq {
-    static constexpr int NS = PERIOD ? 5 * LS : 0;
-    static constexpr int N = NS + 2 * LC + NREAD;
-    static constexpr int mask(int k)
-    {
-        return k < NS ? (k < 4 * LS ? 0x200 : 0x020)
-                      : (k - NS < 2 * LC ? ((k - NS) % 2 == 0 ? 0x200 : 0x020) : 0x100);
-    }
-};
-
-// Interleave request for one stage: NM MFMA slots; slot K holds one MFMA and
-// then its share of the memory operations, in their program order.  The
-// operations all go into the first NMEM slots, so the reads of the next
-// stage have the rest of the stage to land.
-template <int NM, int NMEM, class Ops>
-__device__ __forceinline__ void sched_stage()
-{
-    static_for<NM>([&](auto kc) {
-        constexpr int K = decltype(kc)::value;
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (K < NMEM) {
-            constexpr int k0 = Ops::N * K / NMEM, k1 = Ops::N * (K + 1) / NMEM;
-            static_for<k1 - k0>([&](auto ic) {
-                constexpr int k = k0 + decltype(ic)::value;
-                __builtin_amdgcn_sched_group_barrier(Ops::mask(k), 1, 0);
-            });
-        }
-    });
-}
-
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 template <int F>
@@ -175,6 +146,19 @@ __device__ __forceinline__ v16f mfma32(v8i x, unsigned sx, v8i y, unsigned sy, v
     constexpr int c = FmtTraits<F>::mfma_code;
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, c, c, 0, (int)sx, 0, (int)sy);
 }
+
+// One sub-step's fragments of a wave's tile: the lane's 16 (E2M1) or 32
+// (E4M3) bytes of each A and B subtile, and the step's scale dwords.
+template <int F, int MT, int NT>
+struct TileFrag {
+    u4v a[MT][FmtTraits<F>::nvec], b[NT][FmtTraits<F>::nvec];
+    unsigned sa[MT], sb[NT];
+    __device__ void sa_from(const TileFrag &o)
+    {
+        for (int i = 0; i < MT; ++i) sa[i] = o.sa[i];
+        for (int j = 0; j < NT; ++j) sb[j] = o.sb[j];
+    }
+};
 
 template <int MT, int NT>
 struct TileRegs {
@@ -192,7 +176,14 @@ void mx_gemm_tile(GemmArgs p)
     static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
     using G = TileGeom<F, MT, NT>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
-    __shared__ __attribute__((aligned(1024))) char smem[G::BYTES];
+    // The two code slots and the scale buffers are separate LDS objects: the
+    // compiler then knows that a fragment read of one slot cannot touch what
+    // a direct-to-LDS load still in flight writes into the other, and does
+    // not wait for every outstanding load before each such read (with one
+    // array it did, once per super-stage, which cost a full memory latency).
+    __shared__ __attribute__((aligned(1024))) char slot0[G::SLOT];
+    __shared__ __attribute__((aligned(1024))) char slot1[G::SLOT];
+    __shared__ __attribute__((aligned(1024))) char sbuf[2 * G::SCB];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -230,42 +221,46 @@ void mx_gemm_tile(GemmArgs p)
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(p.sb + (size_t)n0 * p.srow_bytes, part_range(nrows, p.srow_bytes, 4u * p.nsteps));
 
-    const int T = (int)(p.kbytes / G::W);   // stages
+    // super-stages of this workgroup's K range, rounded up to whole periods
+    const int T2 = (int)((p.kbytes + G::SW - 1) / G::SW);
+    const int U = (T2 + G::P - 1) / G::P * G::P;
 
-    // ---- code loads: job j of this wave is 16-row block q = wave + 4j of
-    // [A blocks | B blocks]; lane l holds row l/4, chunk l%4 of the block
-    const unsigned lrow = (unsigned)(lane >> 2), lchunk = (unsigned)(lane & 3);
-    const unsigned vload = lrow * p.row_bytes + 16u * lchunk;
-    const int vwrite = G::code_off(lrow, lchunk);   // within a 16-row block (2 groups)
-    u4v stg[2][G::LC];                               // staging sets (stage parity)
-
-    auto load_one = [&](int j, int t) {
+    // ---- code loads, straight into LDS: load j of this wave is 1 KB block
+    // q = wave + 4j of [A rows | B rows] (8 rows x 128 bytes); lane l takes
+    // row 8q + l/8 and the chunk whose swizzled place is position l%8
+    const int lrow = lane >> 3;
+    unsigned voff[G::LB], cb[G::LB];
+    bool vla[G::LB];
+#pragma unroll
+    for (int j = 0; j < G::LB; ++j) {
         const int q = wave + 4 * j;
-        const bool isa = q < G::BM / 16;
-        const unsigned qrow = 16u * (unsigned)(isa ? q : q - G::BM / 16);
-        const unsigned kadd = t < T ? (unsigned)t * G::W : kOutOfRange;
-        return load16<CPOL_NONE>(isa ? ra : rb, vload + qrow * p.row_bytes + kadd);
+        const int row = 8 * q + lrow;                        // tile row in [A | B]
+        cb[j] = 16u * (unsigned)((lane & 7) ^ ((row >> 1) & 7));   // this lane's chunk, in bytes
+        vla[j] = 8 * q < G::BM;                               // A and B rows never share a block
+        voff[j] = (unsigned)(vla[j] ? row : row - G::BM) * p.row_bytes + cb[j];
+    }
+    const unsigned kb = p.kbytes;
+    // slot of super-stage u: its parity, always known at compile time
+    auto slot_of = [&](auto parity) -> char * {
+        if constexpr (decltype(parity)::value)
+            return slot1;
+        else
+            return slot0;
     };
-    auto write_one = [&](int j, const u4v &v, int t) {
-        const int q = wave + 4 * j;   // block of [A | B]: 16 rows = 2 groups
-        *reinterpret_cast<u4v *>(smem + (t & 1) * G::CODE + q * 2 * G::GROUP + vwrite) = v;
-    };
-    auto code_load = [&](u4v (&dst)[G::LC], int t) {
+    auto code_load = [&](auto parity, int u) {   // super-stage u (of that parity) into its slot
+        char *slot = slot_of(parity);
 #pragma unroll
-        for (int j = 0; j < G::LC; ++j)
-            dst[j] = load_one(j, t);
-    };
-    auto code_write = [&](const u4v (&src)[G::LC], int t) {
-#pragma unroll
-        for (int j = 0; j < G::LC; ++j)
-            write_one(j, src[j], t);
-    };
-    // write stage tw from a staging set, refilling each register with stage tl
-    auto code_cycle = [&](u4v (&set)[G::LC], int tw, int tl) {
-#pragma unroll
-        for (int j = 0; j < G::LC; ++j) {
-            write_one(j, set[j], tw);
-            set[j] = load_one(j, tl);
+        for (int j = 0; j < G::LB; ++j) {
+            const int q = wave + 4 * j;
+            // past this K range: an offset no buffer range reaches (zeros)
+            const unsigned off = (unsigned)u * G::SW + cb[j] < kb ? voff[j] + (unsigned)u * G::SW : kOutOfRange;
+            // (a branch, not a select of the two resources: the latter is
+            // rejected by the host pass of a __global__ template, which
+            // then silently emits no launch stub)
+            if (vla[j])
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * q), 16, off, 0, 0, CPOL_NONE);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + 1024 * q), 16, off, 0, 0, CPOL_NONE);
         }
     };
 
@@ -273,7 +268,7 @@ void mx_gemm_tile(GemmArgs p)
     // [A rows | B rows]; lane l holds row l's 16 bytes of the period
     u4v sstg[G::LS];
     auto scale_load = [&](int period) {
-        const bool live = period * G::P < T;
+        const bool live = period * G::P < U;
 #pragma unroll
         for (int i = 0; i < G::LS; ++i) {
             const int q = wave + 4 * i;
@@ -289,9 +284,9 @@ void mx_gemm_tile(GemmArgs p)
     // Dword d of a period is 128-K step 4*period + d.  Steps past K are
     // written as zero codes: a row's 16-byte load can run into the next
     // row's codes there, and a NaN code would poison the +0 of the padding
-    // stages.
+    // super-stages.
     auto scale_write = [&](int period) {
-        char *buf = smem + G::SC_OFF + (period & 1) * G::SCB;
+        char *buf = sbuf + (period & 1) * G::SCB;
 #pragma unroll
         for (int i = 0; i < G::LS; ++i) {
             const int row = (wave + 4 * i) * 64 + lane;
@@ -302,25 +297,33 @@ void mx_gemm_tile(GemmArgs p)
         }
     };
 
-    // ---- fragment reads: lane (r, g) reads rows wm*32*MT + 32i + r (A) and
-    // wn*32*NT + 32j + r (B), chunk 2h + g
+    // ---- fragments of one sub-step: lane (r, g) reads rows wm*32*MT + 32i
+    // + r (A) and wn*32*NT + 32j + r (B); E2M1 sub-step h is chunk 2h + g,
+    // E4M3 sub-step h chunks 4h + g and 4h + 2 + g; the scale dword is the
+    // 128-K step's
+    constexpr int NV = FmtTraits<F>::nvec;
+    using Frag = TileFrag<F, MT, NT>;
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
-    const int a_lane = G::code_off(arow, g);
-    const int b_lane = G::code_off(brow, g);
-    auto read = [&](TileRegs<MT, NT> &R, int t) {
-        const char *slot = smem + (t & 1) * G::CODE;
-        const char *sc = smem + G::SC_OFF + ((t / G::P) & 1) * G::SCB +
-                         (F == FMT_FP4 ? t % 4 : (t % 8) / 2) * G::SROWS * 4;
+    auto read = [&](Frag &R, auto parity, int u, int h, const Frag *prev) {
+        const char *slot = slot_of(parity);
+        const int step = (u % G::P) * G::STEPS + (F == FMT_FP4 ? h / 2 : 0);   // within the period
+        const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + step * G::SROWS * 4;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int v = 0; v < NV; ++v) {
+            const int c = F == FMT_FP4 ? 2 * h + g : 4 * h + 2 * v + g;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                R.a[i][h] = *reinterpret_cast<const u4v *>(slot + a_lane + 4 * G::GROUP * i + 2 * G::CHUNK * h);
+            for (int i = 0; i < MT; ++i)
+                R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                R.b[j][h] = *reinterpret_cast<const u4v *>(slot + b_lane + 4 * G::GROUP * j + 2 * G::CHUNK * h);
+            for (int j = 0; j < NT; ++j)
+                R.b[j][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(brow + 32 * j, c));
+        }
+        // the two sub-steps of a 128-K step share its scale dword: an odd
+        // sub-step takes it from the even one's registers
+        if (h % 2 == 1) {
+            R.sa_from(*prev);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
             R.sa[i] = *reinterpret_cast<const unsigned *>(sc + 4 * (arow + 32 * i));
@@ -338,93 +341,95 @@ void mx_gemm_tile(GemmArgs p)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.f;
 
-    auto compute = [&](const TileRegs<MT, NT> &R, int t) {
-        if constexpr (F == FMT_FP4) {
+    // sub-step h: blocks 2*(h % 2) + g of the step's scale dword
+    auto compute = [&](const Frag &R, int h) {
+        const unsigned sh = 8u * (2 * (h & 1) + g);
+        unsigned xs[NT], ys[MT];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const unsigned sh = 8u * (2 * s + g);   // block 2s+g of the 128-K dword
-                unsigned xs[NT], ys[MT];
+        for (int j = 0; j < NT; ++j) xs[j] = R.sb[j] >> sh;
 #pragma unroll
-                for (int j = 0; j < NT; ++j) xs[j] = R.sb[j] >> sh;
+        for (int i = 0; i < MT; ++i) ys[i] = R.sa[i] >> sh;
 #pragma unroll
-                for (int i = 0; i < MT; ++i) ys[i] = R.sa[i] >> sh;
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-                for (int i = 0; i < MT; ++i)
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) {
-                        const u4v bx = R.b[j][s], ay = R.a[i][s];
-                        const v8i x = {(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w, 0, 0, 0, 0};
-                        const v8i y = {(int)ay.x, (int)ay.y, (int)ay.z, (int)ay.w, 0, 0, 0, 0};
-                        acc[i][j] = mfma32<F>(x, xs[j], y, ys[i], acc[i][j]);
-                    }
-            }
-        } else {
-            const unsigned sh = 8u * (2 * (t & 1) + g);   // this 64-K stage's half of the dword
-            unsigned xs[NT], ys[MT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) xs[j] = R.sb[j] >> sh;
-#pragma unroll
-            for (int i = 0; i < MT; ++i) ys[i] = R.sa[i] >> sh;
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const u4v b0 = R.b[j][0], b1 = R.b[j][1], a0 = R.a[i][0], a1 = R.a[i][1];
-                    const v8i x = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                                   (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                    const v8i y = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                    acc[i][j] = mfma32<F>(x, xs[j], y, ys[i], acc[i][j]);
+            for (int j = 0; j < NT; ++j) {
+                v8i x, y;
+                if constexpr (F == FMT_FP4) {
+                    const u4v bx = R.b[j][0], ay = R.a[i][0];
+                    x = v8i{(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w, 0, 0, 0, 0};
+                    y = v8i{(int)ay.x, (int)ay.y, (int)ay.z, (int)ay.w, 0, 0, 0, 0};
+                } else {
+                    const u4v b0 = R.b[j][0], b1 = R.b[j][NV - 1], a0 = R.a[i][0], a1 = R.a[i][NV - 1];
+                    x = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                    y = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 }
-        }
+                acc[i][j] = mfma32<F>(x, xs[j], y, ys[i], acc[i][j]);
+            }
     };
 
-    constexpr int NM = (F == FMT_FP4 ? 2 : 1) * MT * NT;   // MFMAs per stage
-    constexpr int NMEM = NM * 3 / 4;
-    constexpr int NREAD = 3 * (MT + NT);                   // fragment and scale reads
-    TileRegs<MT, NT> R[2];
+    constexpr int NM = MT * NT;                  // MFMAs per sub-step
+    constexpr int NCR = NV * (MT + NT);          // fragment reads per sub-step
+    Frag R[2];
 
-    // prologue: scales of periods 0 (written) and 1 (staged); code stages 0
-    // and 1 written to the two slots; stages 2 and 3 staged
+    // prologue: period 0's scale codes written, period 1's staged;
+    // super-stages 0 and 1 requested; super-stage 0's first fragments read
     scale_load(0);
     wait_vm<0>();
     scale_write(0);
+    using even = std::integral_constant<int, 0>;
+    using odd = std::integral_constant<int, 1>;
+    code_load(even{}, 0);
+    code_load(odd{}, 1);
     scale_load(1);
-    code_load(stg[0], 0);
-    code_load(stg[1], 1);
-    wait_vm<0>();
-    code_write(stg[0], 0);
-    code_write(stg[1], 1);
-    code_load(stg[0], 2);
-    code_load(stg[1], 3);
+    wait_vm<G::LB + G::LS>();   // super-stage 0 has landed
     block_barrier();
-    read(R[0], 0);
+    read(R[0], even{}, 0, 0, nullptr);
 
-    // Iteration t (u = t mod P): everything issued two or more iterations
-    // ago has landed; write stage t+2 from its staging set into the slot
-    // stage t used and reload that set with stage t+4; in the second
-    // iteration of a period also write the next period's scale codes (first
-    // read P-2 iterations later) and stage the one after; read stage t+1's
-    // fragments; run stage t's MFMAs.
-    auto iteration = [&](auto uc, int t) {
-        constexpr int u = decltype(uc)::value;
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<G::LC + (u == 2 ? G::LS : 0)>();
-        block_barrier();
-        if constexpr (u == 1) {
-            scale_write(t / G::P + 1);
-            scale_load(t / G::P + 2);
-        }
-        code_cycle(stg[u & 1], t + 2, t + 4);
-        read(R[(u + 1) & 1], t + 1);
-        compute(R[u & 1], t);
-        sched_stage<NM, NMEM, OpSeq<u == 1, G::LS, G::LC, NREAD>>();
-        __builtin_amdgcn_sched_barrier(0);
+    // Iteration u: sub-steps 0 .. SUB-2 read the next sub-step while
+    // computing; before the last one, wait for super-stage u+1, barrier, refill slot u with super-stage u+2 and at a period start
+    // write the next period's scale codes and stage the one after; the
+    // last sub-step reads super-stage u+1's first fragments.
+    auto iteration = [&](auto uc, int u) {
+        static_for<G::SUB>([&](auto hc) {
+            constexpr int pu = decltype(uc)::value;   // u % P
+            constexpr int h = decltype(hc)::value;
+            using mine = std::integral_constant<int, pu & 1>;          // slot of u and u + 2
+            using next = std::integral_constant<int, (pu + 1) & 1>;    // slot of u + 1
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (h == G::SUB - 1) {
+                // super-stage u+1 (and any scale loads issued with it, one
+                // iteration ago) has landed
+                wait_vm<0>();
+                block_barrier();
+                if constexpr (pu == 0)
+                    scale_write(u / G::P + 1);
+                code_load(mine{}, u + 2);
+                if constexpr (pu == 0)
+                    scale_load(u / G::P + 2);
+                read(R[(h + 1) & 1], next{}, u + 1, 0, nullptr);
+            } else {
+                read(R[(h + 1) & 1], mine{}, u, h + 1, &R[h & 1]);
+            }
+            compute(R[h & 1], h);
+            // interleave: each MFMA followed by its share of the memory
+            // operations (loads and scale writes at the last sub-step)
+            constexpr int NMEM = h == G::SUB - 1 ? G::LB + (pu == 0 ? 5 * G::LS : 0) : 0;
+            constexpr int NRD = NCR + ((h + 1) % G::SUB % 2 == 0 ? MT + NT : 0);
+            static_for<NM>([&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                constexpr int r0 = NRD * K / NM, r1 = NRD * (K + 1) / NM;
+                if constexpr (r1 > r0)
+                    __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
+                constexpr int m0 = NMEM * K / NM, m1 = NMEM * (K + 1) / NM;
+                if constexpr (m1 > m0)
+                    __builtin_amdgcn_sched_group_barrier(0x020 | 0x200, m1 - m0, 0);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
-    // Whole periods without branches.  Stages past K (at most P-1 of them)
-    // run on zero codes and zero scale codes, which add exactly +0.
-    for (int t0 = 0; t0 < T; t0 += G::P)
-        static_for<G::P>([&](auto uc) { iteration(uc, t0 + decltype(uc)::value); });
+    for (int u0 = 0; u0 < U; u0 += G::P)
+        static_for<G::P>([&](auto uc) { iteration(uc, u0 + decltype(uc)::value); });
     wait_vm<0>();
 
     // split-K: the K parts of this tile are summed by the last one to finish
@@ -478,8 +483,8 @@ void mx_gemm_tile(GemmArgs p)
         // the (now idle) code slots.
         constexpr int RS = 64 * NT + 16;            // region row stride (bytes, padded)
         constexpr int HR = 16 * MT;                  // rows per pass
-        static_assert(4 * HR * RS <= 2 * G::CODE, "epilogue staging must fit the code slots");
-        char *region = smem + wave * HR * RS;
+        static_assert(2 * HR * RS <= G::SLOT, "epilogue staging must fit the code slots");
+        char *region = (wave < 2 ? slot0 : slot1) + (wave & 1) * HR * RS;
         constexpr int LPR = 4 * NT;                  // lanes per row (16 bytes each)
         constexpr int RPI = 64 / LPR;                // rows per store instruction
         const int lr = lane / LPR, lc = lane % LPR;
