@@ -617,26 +617,47 @@ class GemmRunner:
         self.step = step
         self.alg_bytes = cs.algorithmic_bytes(2) - cs.M * cs.N * (2.0 - self.out_bytes)
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, settle_s=1.0):
         """W warm-up steps, then one call on every rotated set (so that no
-        timed step is the first touch of its set), then exactly `steps`
-        back-to-back timed steps between two HIP events on the launch stream.
-        Returns (ms per step, host enqueue seconds, wall seconds)."""
+        timed step is the first touch of its set), then back-to-back calls
+        for `settle_s` seconds (the shader clock settles under this load
+        within that time; the first milliseconds of a new load run at
+        another clock), then exactly `steps` back-to-back timed steps
+        between two HIP events on the launch stream.  Returns (ms per step,
+        host enqueue seconds, wall seconds)."""
         import torch
         for i in range(warmup):
             self.step(i)
         for i in range(self.R):
             self.step(i)
         torch.cuda.synchronize()
-        # Keep the GPU busy with unrelated work while the host enqueues the
-        # timed steps, so that no step waits for the host: the timed region
-        # holds `steps` back-to-back launches, bracketed by two events on
-        # the launch stream.
-        filler = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            for i in range(16):
+                self.step(n + i)
+            n += 16
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= settle_s:
+                break
+        per_step = (time.perf_counter() - t0) / n
+        self.settle = {"seconds": round(time.perf_counter() - t0, 3), "calls": n}
+        # The timed region must hold `steps` back-to-back launches: the GPU
+        # must never wait for the host.  Calls longer than the host's enqueue
+        # time queue up by themselves behind a few untimed ones; for short
+        # calls a long unrelated kernel keeps the GPU busy while the host
+        # enqueues the timed steps.
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        for _ in range(max(8, steps // 4)):
-            filler.add_(1.0)
+        filler = None
+        self.filler = per_step < 100e-6
+        if self.filler:
+            filler = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+            torch.cuda.synchronize()
+            for _ in range(max(8, steps // 4)):
+                filler.add_(1.0)
+        else:
+            for i in range(4):
+                self.step(i)
         t0 = time.perf_counter()
         ev0.record(self.stream)
         for i in range(steps):
@@ -822,6 +843,8 @@ def main():
         "roofline": roof,
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_s": round(t_enqueue, 4),
+        "settle": runner.settle,
+        "filler_before_timed_region": runner.filler,
     }
     if not args.no_sclk:
         out["sclk"] = sclk_under_load(runner, ms)
@@ -843,6 +866,7 @@ def main():
         rec = {"us_per_call": round(sms * 1e3, 3),
                "value": round(sc.flops / (sms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                "steps": steps, "rotating_sets": r.R, "recipe": sc.recipe,
+               "settle": r.settle, "filler_before_timed_region": r.filler,
                "roofline": r.roofline(sms, name)}
         if name.startswith("c1_"):
             # launch-bound: its roofline time is ns; the reading that means
