@@ -299,20 +299,16 @@ void mx_gemm_decode(GemmArgs p)
         const char *slot = DMA ? ring + u * D::DSLOT : slots + (D::SLOTS == 2 ? (i & 1) * D::SLOT : 0);
         auto boff = [&](int c) { return DMA ? D::d_off(r, c) : D::b_off(r, c); };
         const int t = t0 + i;
-#pragma unroll
-        for (int s = 0; s < D::SPS; ++s) {
-            const int k = t * D::SPS + s;
-            if (k >= nst)
-                break;
-            StepFrag<F> fb, fa[MT];
+        // fragments and scale codes of 128-K step k (the s-th of the stage)
+        auto read_step = [&](int s, int k, StepFrag<F> &fb, StepFrag<F> (&fa)[MT], unsigned &sb,
+                             unsigned (&sa)[MT]) {
             if constexpr (F == FMT_FP4) {
                 fb.d[0] = *reinterpret_cast<const u4v *>(slot + boff(4 * s + g));
             } else {
                 fb.d[0] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + g));
                 fb.d[1] = *reinterpret_cast<const u4v *>(slot + boff(8 * s + 4 + g));
             }
-            const unsigned sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::SBSS + 16 * rw + r)) >> (8 * g);
-            unsigned sa[MT];
+            sb = *reinterpret_cast<const unsigned *>(smem + D::SBS_OFF + 4 * (k * D::SBSS + 16 * rw + r)) >> (8 * g);
 #pragma unroll
             for (int x = 0; x < MT; ++x) {
                 const int row = 16 * x + r;
@@ -324,9 +320,34 @@ void mx_gemm_decode(GemmArgs p)
                 }
                 sa[x] = *reinterpret_cast<const unsigned *>(smem + D::SA_OFF + 4 * (k * D::SAS + row)) >> (8 * g);
             }
+        };
+        if ((t + 1) * D::SPS <= nst) {
+            // a whole stage inside K: every read issued before the first
+            // MFMA, so the LDS round trips of the steps overlap
+            StepFrag<F> fb[D::SPS], fa[D::SPS][MT];
+            unsigned sb[D::SPS], sa[D::SPS][MT];
 #pragma unroll
-            for (int x = 0; x < MT; ++x)
-                acc[x] = mfma<F>(fb, sb, fa[x], sa[x], acc[x]);
+            for (int s = 0; s < D::SPS; ++s)
+                read_step(s, t * D::SPS + s, fb[s], fa[s], sb[s], sa[s]);
+#pragma unroll
+            for (int s = 0; s < D::SPS; ++s)
+#pragma unroll
+                for (int x = 0; x < MT; ++x)
+                    acc[x] = mfma<F>(fb[s], sb[s], fa[s][x], sa[s][x], acc[x]);
+        } else {
+            // the stage that holds the end of K: its steps past K are skipped
+#pragma unroll
+            for (int s = 0; s < D::SPS; ++s) {
+                const int k = t * D::SPS + s;
+                if (k >= nst)
+                    break;
+                StepFrag<F> fb, fa[MT];
+                unsigned sb, sa[MT];
+                read_step(s, k, fb, fa, sb, sa);
+#pragma unroll
+                for (int x = 0; x < MT; ++x)
+                    acc[x] = mfma<F>(fb, sb, fa[x], sa[x], acc[x]);
+            }
         }
         if constexpr (DMA) {
             if (i + G < nt) {
