@@ -45,16 +45,18 @@
 // buffers are separate LDS objects, so the compiler can tell a fragment
 // read of one slot from the loads still landing in the other.
 //
-// Pipeline (iteration u computes super-stage u; two code slots).  Sub-step
-// h's fragments are read while sub-step h-1's MFMAs run.  Before the last
-// sub-step: wait for super-stage u+1's loads, barrier (every wave's loads
-// of u+1 have landed and every wave is done reading slot u), issue the
-// loads of u+2 into slot u, and at a period start write the next period's
-// scale codes and load the one after; the last sub-step's MFMAs then cover
-// the read of super-stage u+1's first fragments.  A load has one iteration
-// to land.  The loop runs whole periods; super-stages past K (and rows past
-// M or N) load zero codes through out-of-range offsets and have zero scale
-// codes, and add exactly +0.
+// Pipeline (iteration u computes super-stage u; NS = 2 or 4 code slots).
+// Sub-step h's fragments are read while sub-step h-1's MFMAs run.  Before
+// the last sub-step: wait for super-stage u+1's loads, barrier (every
+// wave's loads of u+1 have landed and every wave is done reading slot u),
+// issue the loads of u+NS into slot u, and at a period start write the next
+// period's scale codes and load the one after; the last sub-step's MFMAs
+// then cover the read of super-stage u+1's first fragments.  A load has
+// NS-1 iterations to land: four slots where a super-stage is little MFMA
+// work (the 128 x 128 tile: 16 MFMAs per wave, less than an HBM round
+// trip) and LDS allows.  The loop runs whole periods; super-stages past K
+// (and rows past M or N) load zero codes through out-of-range offsets and
+// have zero scale codes, and add exactly +0.
 //
 // Waves.  Four waves in 2 x 2, each owning a (32*MT) x (32*NT) part of the
 // (64*MT) x (64*NT) workgroup tile; at MT = NT = 4 the 256 accumulator
@@ -79,7 +81,7 @@
 
 namespace mxg {
 
-template <int F, int MT, int NT>
+template <int F, int MT, int NT, int NS = 2>
 struct TileGeom {
     static constexpr int BM = 64 * MT, BN = 64 * NT;    // workgroup tile
     static constexpr int ROWS = BM + BN;                 // A rows then B rows
@@ -94,10 +96,16 @@ struct TileGeom {
     static constexpr int LS = cdiv_c(SJOBS, 4);          // per wave (jobs past SJOBS load nothing)
     static constexpr int SROWS = 64 * 4 * LS;            // scale rows incl. padding
     static constexpr int SCB = SROWS * 16;               // one scale buffer: [dword][row]
-    static constexpr int BYTES = 2 * SLOT + 2 * SCB;
+    static constexpr int BYTES = NS * SLOT + 2 * SCB;
+    // super-stages per turn of the loop: whole periods and whole rounds of
+    // the NS code slots, so that both indexes are known at compile time
+    // (with four slots also whole pairs of periods: the scale staging
+    // registers alternate between two sets by period)
+    static constexpr int TURN = NS == 2 ? P : (NS > 2 * P ? NS : 2 * P);
+    static_assert(NS == 2 || NS == 4, "two or four code slots");
     static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
     static_assert((ROWS / 8) % 4 == 0, "load blocks must spread evenly over 4 waves");
-    static_assert(LB + LS < 64, "outstanding loads must fit the vmcnt field");
+    static_assert((NS - 1) * LB + 2 * LS < 64, "outstanding loads must fit the vmcnt field");
     // byte offset of 16-byte chunk c (0..7) of tile row `row` in a code slot
     __device__ static constexpr int code_off(int row, int c)
     {
@@ -169,12 +177,12 @@ struct TileRegs {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0>
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
     static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
-    using G = TileGeom<F, MT, NT>;
+    using G = TileGeom<F, MT, NT, NS>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     // The two code slots and the scale buffers are separate LDS objects: the
     // compiler then knows that a fragment read of one slot cannot touch what
@@ -183,6 +191,8 @@ void mx_gemm_tile(GemmArgs p)
     // array it did, once per super-stage, which cost a full memory latency).
     __shared__ __attribute__((aligned(1024))) char slot0[G::SLOT];
     __shared__ __attribute__((aligned(1024))) char slot1[G::SLOT];
+    __shared__ __attribute__((aligned(1024))) char slot2[NS == 4 ? G::SLOT : 16];
+    __shared__ __attribute__((aligned(1024))) char slot3[NS == 4 ? G::SLOT : 16];
     __shared__ __attribute__((aligned(1024))) char sbuf[2 * G::SCB];
 
     const int lane = threadIdx.x & 63;
@@ -240,15 +250,20 @@ void mx_gemm_tile(GemmArgs p)
         voff[j] = (unsigned)(vla[j] ? row : row - G::BM) * p.row_bytes + cb[j];
     }
     const unsigned kb = p.kbytes;
-    // slot of super-stage u: its parity, always known at compile time
-    auto slot_of = [&](auto parity) -> char * {
-        if constexpr (decltype(parity)::value)
+    // slot of super-stage u: u mod NS, always known at compile time
+    auto slot_of = [&](auto k) -> char * {
+        constexpr int K = decltype(k)::value;
+        if constexpr (K == 3)
+            return slot3;
+        else if constexpr (K == 2)
+            return slot2;
+        else if constexpr (K == 1)
             return slot1;
         else
             return slot0;
     };
-    auto code_load = [&](auto parity, int u) {   // super-stage u (of that parity) into its slot
-        char *slot = slot_of(parity);
+    auto code_load = [&](auto k, int u) {   // super-stage u into slot k = u mod NS
+        char *slot = slot_of(k);
 #pragma unroll
         for (int j = 0; j < G::LB; ++j) {
             const int q = wave + 4 * j;
@@ -266,8 +281,13 @@ void mx_gemm_tile(GemmArgs p)
 
     // ---- scale codes: job i of this wave is 64-row block q = wave + 4i of
     // [A rows | B rows]; lane l holds row l's 16 bytes of the period
-    u4v sstg[G::LS];
-    auto scale_load = [&](int period) {
+    // staging registers of a period's codes: one set, or with four slots
+    // two (a period's codes are then loaded two periods before they are
+    // written, as the code loads may stay in flight for three iterations)
+    constexpr int SSETS = NS == 4 ? 2 : 1;
+    constexpr int SLEAD = NS == 4 ? 3 : 2;   // periods between a period's load and its use
+    u4v sstg[SSETS][G::LS];
+    auto scale_load = [&](auto set, int period) {   // set = period % SSETS
         const bool live = period * G::P < U;
 #pragma unroll
         for (int i = 0; i < G::LS; ++i) {
@@ -278,14 +298,14 @@ void mx_gemm_tile(GemmArgs p)
                                      ? (unsigned)(isa ? row : row - G::BM) * p.srow_bytes +
                                            16u * (unsigned)period
                                      : kOutOfRange;
-            sstg[i] = load16<CPOL_NONE>(isa ? rsa : rsb, off);
+            sstg[decltype(set)::value][i] = load16<CPOL_NONE>(isa ? rsa : rsb, off);
         }
     };
     // Dword d of a period is 128-K step 4*period + d.  Steps past K are
     // written as zero codes: a row's 16-byte load can run into the next
     // row's codes there, and a NaN code would poison the +0 of the padding
     // super-stages.
-    auto scale_write = [&](int period) {
+    auto scale_write = [&](auto set, int period) {   // set = period % SSETS
         char *buf = sbuf + (period & 1) * G::SCB;
 #pragma unroll
         for (int i = 0; i < G::LS; ++i) {
@@ -293,7 +313,7 @@ void mx_gemm_tile(GemmArgs p)
 #pragma unroll
             for (int d = 0; d < 4; ++d)
                 *reinterpret_cast<unsigned *>(buf + d * G::SROWS * 4 + row * 4) =
-                    4 * period + d < p.nsteps ? sstg[i][d] : 0u;
+                    4 * period + d < p.nsteps ? sstg[decltype(set)::value][i][d] : 0u;
         }
     };
 
@@ -304,8 +324,8 @@ void mx_gemm_tile(GemmArgs p)
     constexpr int NV = FmtTraits<F>::nvec;
     using Frag = TileFrag<F, MT, NT>;
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
-    auto read = [&](Frag &R, auto parity, int u, int h, const Frag *prev) {
-        const char *slot = slot_of(parity);
+    auto read = [&](Frag &R, auto k, int u, int h, const Frag *prev) {
+        const char *slot = slot_of(k);
         const int step = (u % G::P) * G::STEPS + (F == FMT_FP4 ? h / 2 : 0);   // within the period
         const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + step * G::SROWS * 4;
 #pragma unroll
@@ -372,40 +392,71 @@ void mx_gemm_tile(GemmArgs p)
     Frag R[2];
 
     // prologue: period 0's scale codes written, period 1's staged;
-    // super-stages 0 and 1 requested; super-stage 0's first fragments read
-    scale_load(0);
+    // super-stages 0 .. NS-1 requested; super-stage 0's first fragments read
+    using set_0 = std::integral_constant<int, 0>;
+    using set_1 = std::integral_constant<int, SSETS - 1>;   // period 1's set
+    scale_load(set_0{}, 0);
     wait_vm<0>();
-    scale_write(0);
-    using even = std::integral_constant<int, 0>;
-    using odd = std::integral_constant<int, 1>;
-    code_load(even{}, 0);
-    code_load(odd{}, 1);
-    scale_load(1);
-    wait_vm<G::LB + G::LS>();   // super-stage 0 has landed
+    scale_write(set_0{}, 0);
+    using slot_0 = std::integral_constant<int, 0>;
+    if constexpr (NS == 4) {
+        // the staging loads first: the loop then starts, as it continues,
+        // with code loads as the most recent ones (the compiler's own wait
+        // bookkeeping merges the two at the loop head)
+        scale_load(set_1{}, 1);
+        scale_load(set_0{}, 2);
+    }
+    code_load(slot_0{}, 0);
+    code_load(std::integral_constant<int, 1>{}, 1);
+    if constexpr (NS == 4) {
+        code_load(std::integral_constant<int, 2>{}, 2);
+        code_load(std::integral_constant<int, 3>{}, 3);
+        wait_vm<(NS - 1) * G::LB>();   // super-stage 0 has landed
+    } else {
+        scale_load(set_1{}, 1);
+        wait_vm<G::LB + G::LS>();      // super-stage 0 has landed
+    }
     block_barrier();
-    read(R[0], even{}, 0, 0, nullptr);
+    read(R[0], slot_0{}, 0, 0, nullptr);
 
     // Iteration u: sub-steps 0 .. SUB-2 read the next sub-step while
-    // computing; before the last one, wait for super-stage u+1, barrier, refill slot u with super-stage u+2 and at a period start
-    // write the next period's scale codes and stage the one after; the
-    // last sub-step reads super-stage u+1's first fragments.
+    // computing; before the last one, wait for super-stage u+1, barrier,
+    // refill slot u with super-stage u+NS and at a period start write the
+    // next period's scale codes and stage the one after; the last sub-step
+    // reads super-stage u+1's first fragments.
     auto iteration = [&](auto uc, int u) {
+        constexpr int i = decltype(uc)::value;   // u % TURN
+        constexpr int pu = i % G::P;             // u % P
+        using mine = std::integral_constant<int, i % NS>;         // slot of u and u + NS
+        using next = std::integral_constant<int, (i + 1) % NS>;   // slot of u + 1
+        // loads issued after super-stage u+1's, which may stay in flight
+        // while it is waited for: the code loads of u+2 .. u+NS-1 and the
+        // scale loads issued with those and with u+1's (iterations
+        // u+1-NS .. u-1 that start a period); early on the count is lower
+        // than what is in flight, which only waits longer
+        constexpr int AFTER = NS == 2 ? 0 : [] {
+            int n = (NS - 2) * G::LB;
+            for (int j = i + 1 - NS; j <= i - 1; ++j)
+                if (((j % G::P) + G::P) % G::P == 0)
+                    n += G::LS;
+            return n;
+        }();
         static_for<G::SUB>([&](auto hc) {
-            constexpr int pu = decltype(uc)::value;   // u % P
             constexpr int h = decltype(hc)::value;
-            using mine = std::integral_constant<int, pu & 1>;          // slot of u and u + 2
-            using next = std::integral_constant<int, (pu + 1) & 1>;    // slot of u + 1
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (h == G::SUB - 1) {
-                // super-stage u+1 (and any scale loads issued with it, one
-                // iteration ago) has landed
-                wait_vm<0>();
+                // super-stage u+1 (and any scale loads issued before it) has landed
+                wait_vm<AFTER>();
                 block_barrier();
+                // period of u: u0 / P + i / P with u0 / P a multiple of
+                // SSETS, so the staging set of any period is known here
+                using wset = std::integral_constant<int, (i / G::P + 1) % SSETS>;
+                using lset = std::integral_constant<int, (i / G::P + SLEAD) % SSETS>;
                 if constexpr (pu == 0)
-                    scale_write(u / G::P + 1);
-                code_load(mine{}, u + 2);
+                    scale_write(wset{}, u / G::P + 1);
+                code_load(mine{}, u + NS);
                 if constexpr (pu == 0)
-                    scale_load(u / G::P + 2);
+                    scale_load(lset{}, u / G::P + SLEAD);
                 read(R[(h + 1) & 1], next{}, u + 1, 0, nullptr);
             } else {
                 read(R[(h + 1) & 1], mine{}, u, h + 1, &R[h & 1]);
@@ -428,8 +479,22 @@ void mx_gemm_tile(GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    for (int u0 = 0; u0 < U; u0 += G::P)
-        static_for<G::P>([&](auto uc) { iteration(uc, u0 + decltype(uc)::value); });
+    // whole turns (no branch inside one, so the compiler's own wait
+    // bookkeeping stays exact), then the period left when a turn is two
+    int u0 = 0;
+    for (; u0 + G::TURN <= U; u0 += G::TURN)
+        static_for<G::TURN>([&](auto uc) { iteration(uc, u0 + decltype(uc)::value); });
+    if constexpr (G::TURN > G::P) {
+        // the periods left: fewer than a turn's
+        static_for<G::TURN / G::P - 1>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            if (u0 + q * G::P < U)
+                static_for<G::P>([&](auto uc) {
+                    constexpr int i = q * G::P + decltype(uc)::value;
+                    iteration(std::integral_constant<int, i>{}, u0 + i);
+                });
+        });
+    }
     wait_vm<0>();
 
     // split-K: the K parts of this tile are summed by the last one to finish

@@ -80,13 +80,14 @@ constexpr int ring_depth(int fmt, int mt, int wn)
     {NAME, 32 * (MT), 32 * (NT), 64 * (KW),                                         \
      {MXG_KOUTS(FMT_FP8, MT, NT, KW, G), MXG_KOUTS(FMT_FP4, MT, NT, KW, G)}, {0, 0}, 0, 0}
 
-// Large tiles on the 32x32x64 instruction, staged through registers.
-#define MXG_TFN(F, MT, NT, O) (&mx_gemm_tile<F, MT, NT, O>)
-#define MXG_TOUTS(F, MT, NT) \
-    {MXG_TFN(F, MT, NT, OUT_BF16), MXG_TFN(F, MT, NT, OUT_F16), MXG_TFN(F, MT, NT, OUT_F32)}
-#define MXG_TILE(NAME, MT, NT)                                                      \
+// Large tiles on the 32x32x64 instruction, loaded straight into LDS; NS
+// code slots (four: three super-stages of prefetch).
+#define MXG_TFN(F, MT, NT, NS, O) (&mx_gemm_tile<F, MT, NT, O, 0, 0, NS>)
+#define MXG_TOUTS(F, MT, NT, NS) \
+    {MXG_TFN(F, MT, NT, NS, OUT_BF16), MXG_TFN(F, MT, NT, NS, OUT_F16), MXG_TFN(F, MT, NT, NS, OUT_F32)}
+#define MXG_TILE(NAME, MT, NT, NS)                                                  \
     {NAME, 64 * (MT), 64 * (NT), 256,                                               \
-     {MXG_TOUTS(FMT_FP8, MT, NT), MXG_TOUTS(FMT_FP4, MT, NT)}, {0, 0}, 1, 1}
+     {MXG_TOUTS(FMT_FP8, MT, NT, NS), MXG_TOUTS(FMT_FP4, MT, NT, NS)}, {0, 0}, 1, 1}
 
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
@@ -107,10 +108,12 @@ const Variant kVariants[] = {
 
     MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
 
-    MXG_TILE("tile_256x256",      4, 4),
-    MXG_TILE("tile_256x128",      4, 2),
-    MXG_TILE("tile_128x256",      2, 4),
-    MXG_TILE("tile_128x128",      2, 2),
+    //        name                MT NT NS
+    MXG_TILE("tile_256x256",      4, 4, 2),
+    MXG_TILE("tile_256x128",      4, 2, 2),
+    MXG_TILE("tile_128x256",      2, 4, 2),
+    MXG_TILE("tile_128x128",      2, 2, 2),
+    MXG_TILE("tile_128x128_r4",   2, 2, 4),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -359,7 +362,12 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant("tile_128x256");
     if (M > 128 && cdiv(M, 256) * cdiv(N, 128) >= 192)
         return find_variant("tile_256x128");
-    return find_variant("tile_128x128");
+    // the 128 x 128 tile's super-stage is little MFMA work: over a long K a
+    // ring of four code slots keeps its loads in flight across three of
+    // them (128 x 25600 x 5120 E2M1: 32.3 -> 26.6 us; 512 x 4096 x 4096
+    // E4M3: 25.2 -> 21.9), at short K the two-slot ring starts sooner
+    // (333 x 517 x 1152: 9.0 against 10.1)
+    return find_variant(K >= 4096 ? "tile_128x128_r4" : "tile_128x128");
 }
 
 struct Config {

@@ -347,8 +347,9 @@ DEFAULTS = [
     (1, 128, 4096, 14336, "stream_4x2_k8"),
     (0, 128, 4096, 4096, "stream_4x2_k8"),
     (1, 256, 4096, 4096, "stream_4x4_k4"),
-    (1, 128, 14336, 4096, "tile_128x128"),
-    (1, 128, 25600, 5120, "tile_128x128"),     # no half-empty 256-row tiles
+    (1, 128, 14336, 4096, "tile_128x128_r4"),
+    (1, 128, 25600, 5120, "tile_128x128_r4"),  # no half-empty 256-row tiles; four slots over a long K
+    (1, 333, 517, 1152, "tile_128x128"),       # two slots at short K
     (1, 256, 28672, 8192, "tile_128x256"),
     (0, 256, 28672, 8192, "tile_128x256"),
     (1, 8192, 8192, 8192, "tile_256x256"),
@@ -373,8 +374,8 @@ def test_default_variant_choice(lib, is4, M, N, K, name):
 # MI355X (few output tiles over a long K), the whole-K choice elsewhere.
 SPLIT_DEFAULTS = [
     # (is_fp4, M, N, K, variant, K parts)
-    (1, 512, 4096, 14336, "tile_128x128", 2),
-    (1, 512, 4096, 4096, "tile_128x128", 1),
+    (1, 512, 4096, 14336, "tile_128x128_r4", 2),
+    (1, 512, 4096, 4096, "tile_128x128_r4", 1),
     (1, 32, 4096, 14336, "stream_2x4_k8", 4),
     (1, 32, 4096, 4096, "stream_2x1_k4", 1),
     (1, 32, 14336, 4096, "decode_32x64", 1),
