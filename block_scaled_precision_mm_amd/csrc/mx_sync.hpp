@@ -31,6 +31,19 @@ __device__ __forceinline__ void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same wait as an s_waitcnt the compiler sees (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maximum): its own
+// bookkeeping of outstanding loads then knows what has landed and adds no
+// wait of its own for them.  The empty asm keeps memory accesses on their
+// side of it.
+template <int N>
+__device__ __forceinline__ void wait_vm_known()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier without the implicit memory fence of __syncthreads (which
 // would wait for every outstanding load, including later stages).  The
 // wave's own LDS reads are complete first, so a slot is never refilled

@@ -15,35 +15,40 @@
 // The kernel passes B rows as X and A rows as Y, so lane (r, g) holds
 // C[m0 + r][n0 + 8v + 4g + e]: four runs of four consecutive columns.
 //
-// Super-stages.  The K loop advances 128 bytes of every tile row at a time:
-// 256 K values of E2M1 (four MFMA sub-steps) or 128 of E4M3 (two).  What
-// decided the width, measured on MI355X at 8192^3 E2M1 with loads alone
-// (every workgroup streaming its 256 + 256 rows from L2): 16-byte loads in
-// which 8 lanes read one row's 128 contiguous bytes move the operands at
-// 25.6 TB/s over the chip, against 15.2 TB/s when 4 lanes read 64 bytes of
-// a row (each L1 request then covers half a cache line, and the number of
-// requests in flight, not bytes, sets the rate); loads straight into LDS
-// stream as fast as loads into registers (26.5 TB/s).  What the loop waits
-// on is LDS: fragment reads run at 124 B per clock per compute unit in this
-// layout (measured), and a 128 x 128 wave tile reads 512 bytes of
-// fragments per MFMA besides the 256 bytes the loads write.
+// Super-stages.  The K loop advances SW bytes of every tile row at a time:
+// with SW = 128, 256 K values of E2M1 (four MFMA sub-steps) or 128 of E4M3
+// (two); with SW = 64 half of that.  What decided the width, measured on
+// MI355X at 8192^3 E2M1 with loads alone (every workgroup streaming its
+// 256 + 256 rows from L2): 16-byte loads in which 8 lanes read one row's
+// 128 contiguous bytes move the operands at 25.6 TB/s over the chip,
+// against 15.2 TB/s when 4 lanes read 64 bytes of a row (each L1 request
+// then covers half a cache line, and the number of requests in flight, not
+// bytes, sets the rate); loads straight into LDS stream as fast as loads
+// into registers (26.5 TB/s).  A copy of the loop whose loads touch no
+// memory (out-of-range offsets: same LDS traffic and MFMAs) runs 8192^3 in
+// 189-214 us against 270-298, and 256 x 28672 x 8192 E4M3 in 48 against
+// 97: the super-stage's loads do not land within one super-stage of MFMA
+// work.  Deeper prefetch needs more slots, and LDS holds two 128-byte slots
+// of the largest tiles or four 64-byte ones: E4M3 gains from the latter
+// (2048 x 4096 x 4096 61.5 -> 50.5 us), E2M1 loses (8192^3 +5%: the
+// half-line loads), and the 128 x 128 tile holds four 128-byte slots.
 //
 // Data path.  Global -> LDS directly (gfx950's 16-byte buffer load to LDS:
 // no staging registers, no LDS store instructions).  A load instruction
-// fills 1 KB of LDS in lane order: 8 rows x 128 bytes, lane l at 16*l, so
-// lane l (row l/8 of its block, position p = l%8) fetches the row's chunk
-// c = p ^ s(row), s(row) = (row >> 1) & 7: the 8 lanes of a row still read
-// its 128 contiguous bytes, and chunk c of row `row` sits at
-// 128*row + 16*(c ^ s(row)).  A fragment read (16 consecutive lanes = 16
-// consecutive rows, one chunk) then touches 16 different 16-byte bank
-// groups: the rows alternate between the two 128-byte halves of the 256
-// bytes the LDS banks cover, and s() spreads the 8 rows of each half.
-// Scale codes: 16 bytes per row per period of four 128-K steps, through
-// registers, stored transposed ([step][row] dwords), so an MFMA's scale
-// operand is one dword read plus a shift; the two sub-steps of a 128-K
-// step share the dword (read once).  The two code slots and the scale
+// fills 1 KB of LDS in lane order: 8 rows x 128 bytes (SW = 128) or 16 rows
+// x 64 bytes, lane l at 16*l, so lane l (row l/LPR of its block, position
+// p = l%LPR, LPR = SW/16 lanes per row) fetches the row's chunk
+// c = p ^ s(row): the lanes of a row still read its SW contiguous bytes,
+// and chunk c of row `row` sits at SW*row + 16*(c ^ s(row)).  With
+// s(row) = (row >> 1) & 7 (SW = 128) or (row >> 2) & 3 (SW = 64), a
+// fragment read (16 consecutive lanes = 16 consecutive rows, one chunk)
+// touches 16 different 16-byte bank groups of the 256 bytes the LDS banks
+// cover.  Scale codes: 16 bytes per row per period of four 128-K steps,
+// through registers, stored transposed ([step][row] dwords), so an MFMA's
+// scale operand is one dword read plus a shift; the two sub-steps of a
+// 128-K step share the dword (read once).  The code slots and the scale
 // buffers are separate LDS objects, so the compiler can tell a fragment
-// read of one slot from the loads still landing in the other.
+// read of one slot from the loads still landing in another.
 //
 // Pipeline (iteration u computes super-stage u; NS = 2 or 4 code slots).
 // Sub-step h's fragments are read while sub-step h-1's MFMAs run.  Before
@@ -81,36 +86,54 @@
 
 namespace mxg {
 
-template <int F, int MT, int NT, int NS = 2>
+template <int F, int MT, int NT, int NS = 2, int SW_ = 128>
 struct TileGeom {
     static constexpr int BM = 64 * MT, BN = 64 * NT;    // workgroup tile
     static constexpr int ROWS = BM + BN;                 // A rows then B rows
-    static constexpr int SW = 128;                       // row bytes per super-stage
-    static constexpr int SUB = F == FMT_FP4 ? 4 : 2;     // 32x32x64 sub-steps per super-stage
-    static constexpr int STEPS = F == FMT_FP4 ? 2 : 1;   // 128-K steps per super-stage
+    static constexpr int SW = SW_;                       // row bytes per super-stage (128 or 64)
+    static constexpr int KSS = SW * (F == FMT_FP4 ? 2 : 1);   // K values per super-stage
+    static constexpr int SUB = KSS / 64;                 // 32x32x64 sub-steps per super-stage
     static constexpr int SLOT = ROWS * SW;               // one code slot (unpadded, swizzled)
-    static constexpr int LB = ROWS / 8 / 4;              // 1 KB loads per wave per super-stage
-    // scale codes: 16 bytes per row per period of 4 steps
-    static constexpr int P = 4 / STEPS;                  // super-stages per period
+    static constexpr int RPL = 1024 / SW;                // rows per 1 KB load
+    static constexpr int LPR = SW / 16;                  // lanes per row of a load
+    static constexpr int LB = ROWS / RPL / 4;            // 1 KB loads per wave per super-stage
+    // scale codes: 16 bytes per row per period of 4 steps (512 K)
+    static constexpr int P = 512 / KSS;                  // super-stages per period
     static constexpr int SJOBS = cdiv_c(ROWS, 64);       // 64-row scale loads per period
     static constexpr int LS = cdiv_c(SJOBS, 4);          // per wave (jobs past SJOBS load nothing)
     static constexpr int SROWS = 64 * 4 * LS;            // scale rows incl. padding
     static constexpr int SCB = SROWS * 16;               // one scale buffer: [dword][row]
     static constexpr int BYTES = NS * SLOT + 2 * SCB;
-    // super-stages per turn of the loop: whole periods and whole rounds of
-    // the NS code slots, so that both indexes are known at compile time
-    // (with four slots also whole pairs of periods: the scale staging
-    // registers alternate between two sets by period)
-    static constexpr int TURN = NS == 2 ? P : (NS > 2 * P ? NS : 2 * P);
+    // A period's scale codes are staged in registers between their load and
+    // their write to LDS; with loads in flight for NS-1 iterations they need
+    // a lead of more than one period when a period is shorter than that,
+    // and then two staging sets that alternate by period.
+    static constexpr int SSETS = P >= NS - 1 ? 1 : 2;
+    static constexpr int SLEAD = SSETS == 2 ? 3 : 2;     // periods from a period's load to its write
+    // super-stages per turn of the loop: whole periods, whole rounds of the
+    // NS code slots and (two staging sets) whole pairs of periods, so that
+    // every index is known at compile time
+    static constexpr int TURN = [] {
+        const int per = SSETS * P;
+        return per % NS == 0 ? per : (NS % per == 0 ? NS : per * NS);
+    }();
     static_assert(NS == 2 || NS == 4, "two or four code slots");
+    static_assert(SW == 128 || SW == 64, "super-stages of 64 or 128 bytes per row");
     static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
-    static_assert((ROWS / 8) % 4 == 0, "load blocks must spread evenly over 4 waves");
+    static_assert((ROWS / RPL) % 4 == 0, "load blocks must spread evenly over 4 waves");
+    static_assert(BM % RPL == 0, "A and B rows never share a load block");
     static_assert((NS - 1) * LB + 2 * LS < 64, "outstanding loads must fit the vmcnt field");
-    // byte offset of 16-byte chunk c (0..7) of tile row `row` in a code slot
+    // byte offset of 16-byte chunk c of tile row `row` in a code slot: the
+    // chunk's place XORed with the row so that the 16 rows of a fragment
+    // read fall on 16 different 16-byte bank groups
     __device__ static constexpr int code_off(int row, int c)
     {
-        return row * SW + 16 * (c ^ ((row >> 1) & 7));
+        if constexpr (SW == 128)
+            return row * 128 + 16 * (c ^ ((row >> 1) & 7));
+        else
+            return row * 64 + 16 * (c ^ ((row >> 2) & 3));
     }
+    __device__ static constexpr int swz(int row) { return SW == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
 };
 
 // Linear workgroup index -> position in tile order: workgroups b, b + 8,
@@ -177,12 +200,12 @@ struct TileRegs {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2>
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2, int SW = 128>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
     static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
-    using G = TileGeom<F, MT, NT, NS>;
+    using G = TileGeom<F, MT, NT, NS, SW>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     // The two code slots and the scale buffers are separate LDS objects: the
     // compiler then knows that a fragment read of one slot cannot touch what
@@ -236,17 +259,17 @@ void mx_gemm_tile(GemmArgs p)
     const int U = (T2 + G::P - 1) / G::P * G::P;
 
     // ---- code loads, straight into LDS: load j of this wave is 1 KB block
-    // q = wave + 4j of [A rows | B rows] (8 rows x 128 bytes); lane l takes
-    // row 8q + l/8 and the chunk whose swizzled place is position l%8
-    const int lrow = lane >> 3;
+    // q = wave + 4j of [A rows | B rows] (RPL rows x SW bytes); lane l takes
+    // row RPL*q + l/LPR and the chunk whose swizzled place is position l%LPR
+    const int lrow = lane / G::LPR;
     unsigned voff[G::LB], cb[G::LB];
     bool vla[G::LB];
 #pragma unroll
     for (int j = 0; j < G::LB; ++j) {
         const int q = wave + 4 * j;
-        const int row = 8 * q + lrow;                        // tile row in [A | B]
-        cb[j] = 16u * (unsigned)((lane & 7) ^ ((row >> 1) & 7));   // this lane's chunk, in bytes
-        vla[j] = 8 * q < G::BM;                               // A and B rows never share a block
+        const int row = G::RPL * q + lrow;                    // tile row in [A | B]
+        cb[j] = 16u * (unsigned)((lane % G::LPR) ^ G::swz(row));   // this lane's chunk, in bytes
+        vla[j] = G::RPL * q < G::BM;                          // A and B rows never share a block
         voff[j] = (unsigned)(vla[j] ? row : row - G::BM) * p.row_bytes + cb[j];
     }
     const unsigned kb = p.kbytes;
@@ -281,11 +304,8 @@ void mx_gemm_tile(GemmArgs p)
 
     // ---- scale codes: job i of this wave is 64-row block q = wave + 4i of
     // [A rows | B rows]; lane l holds row l's 16 bytes of the period
-    // staging registers of a period's codes: one set, or with four slots
-    // two (a period's codes are then loaded two periods before they are
-    // written, as the code loads may stay in flight for three iterations)
-    constexpr int SSETS = NS == 4 ? 2 : 1;
-    constexpr int SLEAD = NS == 4 ? 3 : 2;   // periods between a period's load and its use
+    // staging registers of a period's codes (G::SSETS sets, see TileGeom)
+    constexpr int SSETS = G::SSETS, SLEAD = G::SLEAD;
     u4v sstg[SSETS][G::LS];
     auto scale_load = [&](auto set, int period) {   // set = period % SSETS
         const bool live = period * G::P < U;
@@ -318,16 +338,18 @@ void mx_gemm_tile(GemmArgs p)
     };
 
     // ---- fragments of one sub-step: lane (r, g) reads rows wm*32*MT + 32i
-    // + r (A) and wn*32*NT + 32j + r (B); E2M1 sub-step h is chunk 2h + g,
-    // E4M3 sub-step h chunks 4h + g and 4h + 2 + g; the scale dword is the
-    // 128-K step's
+    // + r (A) and wn*32*NT + 32j + r (B); E2M1 sub-step h of a super-stage
+    // is chunk 2h + g, E4M3 sub-step h chunks 4h + g and 4h + 2 + g.  kk is
+    // the sub-step's 64-K index within its period: its scale dword is that
+    // of 128-K step kk / 2.
     constexpr int NV = FmtTraits<F>::nvec;
     using Frag = TileFrag<F, MT, NT>;
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
-    auto read = [&](Frag &R, auto k, int u, int h, const Frag *prev) {
+    auto read = [&](Frag &R, auto k, int u, auto kkc, const Frag *prev) {
+        constexpr int kk = decltype(kkc)::value;
+        constexpr int h = kk % G::SUB;
         const char *slot = slot_of(k);
-        const int step = (u % G::P) * G::STEPS + (F == FMT_FP4 ? h / 2 : 0);   // within the period
-        const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + step * G::SROWS * 4;
+        const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + (kk / 2) * G::SROWS * 4;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int c = F == FMT_FP4 ? 2 * h + g : 4 * h + 2 * v + g;
@@ -340,7 +362,7 @@ void mx_gemm_tile(GemmArgs p)
         }
         // the two sub-steps of a 128-K step share its scale dword: an odd
         // sub-step takes it from the even one's registers
-        if (h % 2 == 1) {
+        if constexpr (kk % 2 == 1) {
             R.sa_from(*prev);
             return;
         }
@@ -361,9 +383,9 @@ void mx_gemm_tile(GemmArgs p)
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0.f;
 
-    // sub-step h: blocks 2*(h % 2) + g of the step's scale dword
-    auto compute = [&](const Frag &R, int h) {
-        const unsigned sh = 8u * (2 * (h & 1) + g);
+    // the half of a 128-K step: blocks 2*half + g of the step's scale dword
+    auto compute = [&](const Frag &R, int half) {
+        const unsigned sh = 8u * (2 * half + g);
         unsigned xs[NT], ys[MT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) xs[j] = R.sb[j] >> sh;
@@ -391,38 +413,38 @@ void mx_gemm_tile(GemmArgs p)
     constexpr int NCR = NV * (MT + NT);          // fragment reads per sub-step
     Frag R[2];
 
-    // prologue: period 0's scale codes written, period 1's staged;
+    // prologue: period 0's scale codes written, the next staged;
     // super-stages 0 .. NS-1 requested; super-stage 0's first fragments read
     using set_0 = std::integral_constant<int, 0>;
-    using set_1 = std::integral_constant<int, SSETS - 1>;   // period 1's set
+    using slot_0 = std::integral_constant<int, 0>;
+    using kk_0 = std::integral_constant<int, 0>;
     scale_load(set_0{}, 0);
     wait_vm<0>();
     scale_write(set_0{}, 0);
-    using slot_0 = std::integral_constant<int, 0>;
-    if constexpr (NS == 4) {
+    if constexpr (NS == 2) {
+        code_load(slot_0{}, 0);
+        code_load(std::integral_constant<int, 1>{}, 1);
+        scale_load(std::integral_constant<int, 1 % SSETS>{}, 1);
+        wait_vm<G::LB + G::LS>();      // super-stage 0 has landed
+    } else {
         // the staging loads first: the loop then starts, as it continues,
         // with code loads as the most recent ones (the compiler's own wait
         // bookkeeping merges the two at the loop head)
-        scale_load(set_1{}, 1);
-        scale_load(set_0{}, 2);
-    }
-    code_load(slot_0{}, 0);
-    code_load(std::integral_constant<int, 1>{}, 1);
-    if constexpr (NS == 4) {
-        code_load(std::integral_constant<int, 2>{}, 2);
-        code_load(std::integral_constant<int, 3>{}, 3);
-        wait_vm<(NS - 1) * G::LB>();   // super-stage 0 has landed
-    } else {
-        scale_load(set_1{}, 1);
-        wait_vm<G::LB + G::LS>();      // super-stage 0 has landed
+        static_for<SLEAD - 1>([&](auto pc) {
+            constexpr int q = 1 + decltype(pc)::value;
+            scale_load(std::integral_constant<int, q % SSETS>{}, q);
+        });
+        __builtin_amdgcn_sched_barrier(0);   // (the scheduler keeps that order)
+        static_for<NS>([&](auto sc) { code_load(sc, decltype(sc)::value); });
+        wait_vm_known<(NS - 1) * G::LB>();   // super-stage 0 has landed
     }
     block_barrier();
-    read(R[0], slot_0{}, 0, 0, nullptr);
+    read(R[0], slot_0{}, 0, kk_0{}, nullptr);
 
     // Iteration u: sub-steps 0 .. SUB-2 read the next sub-step while
     // computing; before the last one, wait for super-stage u+1, barrier,
     // refill slot u with super-stage u+NS and at a period start write the
-    // next period's scale codes and stage the one after; the last sub-step
+    // next period's scale codes and stage a later one; the last sub-step
     // reads super-stage u+1's first fragments.
     auto iteration = [&](auto uc, int u) {
         constexpr int i = decltype(uc)::value;   // u % TURN
@@ -443,12 +465,18 @@ void mx_gemm_tile(GemmArgs p)
         }();
         static_for<G::SUB>([&](auto hc) {
             constexpr int h = decltype(hc)::value;
+            constexpr int kk = pu * G::SUB + h;              // this sub-step within the period
+            constexpr int fb = (i * G::SUB + h) & 1;         // its fragment buffer
             __builtin_amdgcn_sched_barrier(0);
+            constexpr int kn = h == G::SUB - 1 ? (pu + 1) % G::P * G::SUB : kk + 1;   // the next one's
             if constexpr (h == G::SUB - 1) {
                 // super-stage u+1 (and any scale loads issued before it) has landed
-                wait_vm<AFTER>();
+                if constexpr (NS == 2)
+                    wait_vm<AFTER>();
+                else
+                    wait_vm_known<AFTER>();
                 block_barrier();
-                // period of u: u0 / P + i / P with u0 / P a multiple of
+                // the period of u is u0 / P + i / P with u0 / P a multiple of
                 // SSETS, so the staging set of any period is known here
                 using wset = std::integral_constant<int, (i / G::P + 1) % SSETS>;
                 using lset = std::integral_constant<int, (i / G::P + SLEAD) % SSETS>;
@@ -457,15 +485,15 @@ void mx_gemm_tile(GemmArgs p)
                 code_load(mine{}, u + NS);
                 if constexpr (pu == 0)
                     scale_load(lset{}, u / G::P + SLEAD);
-                read(R[(h + 1) & 1], next{}, u + 1, 0, nullptr);
+                read(R[fb ^ 1], next{}, u + 1, std::integral_constant<int, kn>{}, &R[fb]);
             } else {
-                read(R[(h + 1) & 1], mine{}, u, h + 1, &R[h & 1]);
+                read(R[fb ^ 1], mine{}, u, std::integral_constant<int, kn>{}, &R[fb]);
             }
-            compute(R[h & 1], h);
+            compute(R[fb], kk % 2);
             // interleave: each MFMA followed by its share of the memory
             // operations (loads and scale writes at the last sub-step)
             constexpr int NMEM = h == G::SUB - 1 ? G::LB + (pu == 0 ? 5 * G::LS : 0) : 0;
-            constexpr int NRD = NCR + ((h + 1) % G::SUB % 2 == 0 ? MT + NT : 0);
+            constexpr int NRD = NCR + (kn % 2 == 0 ? MT + NT : 0);
             static_for<NM>([&](auto kc) {
                 constexpr int K = decltype(kc)::value;
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -480,12 +508,11 @@ void mx_gemm_tile(GemmArgs p)
         });
     };
     // whole turns (no branch inside one, so the compiler's own wait
-    // bookkeeping stays exact), then the period left when a turn is two
+    // bookkeeping stays exact), then the periods left
     int u0 = 0;
     for (; u0 + G::TURN <= U; u0 += G::TURN)
         static_for<G::TURN>([&](auto uc) { iteration(uc, u0 + decltype(uc)::value); });
     if constexpr (G::TURN > G::P) {
-        // the periods left: fewer than a turn's
         static_for<G::TURN / G::P - 1>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             if (u0 + q * G::P < U)
@@ -548,8 +575,13 @@ void mx_gemm_tile(GemmArgs p)
         // the (now idle) code slots.
         constexpr int RS = 64 * NT + 16;            // region row stride (bytes, padded)
         constexpr int HR = 16 * MT;                  // rows per pass
-        static_assert(2 * HR * RS <= G::SLOT, "epilogue staging must fit the code slots");
-        char *region = (wave < 2 ? slot0 : slot1) + (wave & 1) * HR * RS;
+        // two waves per slot with two slots, one per slot with four
+        static_assert((NS == 2 ? 2 : 1) * HR * RS <= G::SLOT, "epilogue staging must fit the code slots");
+        char *region;
+        if constexpr (NS == 2)
+            region = (wave < 2 ? slot0 : slot1) + (wave & 1) * HR * RS;
+        else
+            region = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
         constexpr int LPR = 4 * NT;                  // lanes per row (16 bytes each)
         constexpr int RPI = 64 / LPR;                // rows per store instruction
         const int lr = lane / LPR, lc = lane % LPR;
