@@ -453,13 +453,17 @@ void mx_gemm_tile(GemmArgs p)
         using next = std::integral_constant<int, (i + 1) % NS>;   // slot of u + 1
         // loads issued after super-stage u+1's, which may stay in flight
         // while it is waited for: the code loads of u+2 .. u+NS-1 and the
-        // scale loads issued with those and with u+1's (iterations
-        // u+1-NS .. u-1 that start a period); early on the count is lower
-        // than what is in flight, which only waits longer
+        // scale loads issued with those (iterations u+2-NS .. u-1 that start
+        // a period).  Not counted, since counting too few only waits longer
+        // while counting one too many races with a load still landing: the
+        // scale loads issued in the same iteration as u+1's code loads (the
+        // scheduler may put them on either side of those), and those of
+        // iterations before this turn (in the first turn there are none:
+        // the prologue issues its scale loads before its code loads).
         constexpr int AFTER = NS == 2 ? 0 : [] {
             int n = (NS - 2) * G::LB;
-            for (int j = i + 1 - NS; j <= i - 1; ++j)
-                if (((j % G::P) + G::P) % G::P == 0)
+            for (int j = i + 2 - NS > 0 ? i + 2 - NS : 0; j <= i - 1; ++j)
+                if (j % G::P == 0)
                     n += G::LS;
             return n;
         }();
@@ -571,10 +575,13 @@ void mx_gemm_tile(GemmArgs p)
         // 16-bit output goes through LDS: in the accumulator layout one store
         // instruction would touch 32 rows (32 cache lines); transposed, each
         // instruction writes whole row segments of the wave's tile.  Two
-        // passes of half the wave's rows; each wave uses its own region of
-        // the (now idle) code slots.
+        // passes of half the wave's rows (one pass when the wave has a single
+        // row of 32x32 tiles); each wave uses its own region of the (now
+        // idle) code slots.
         constexpr int RS = 64 * NT + 16;            // region row stride (bytes, padded)
-        constexpr int HR = 16 * MT;                  // rows per pass
+        constexpr int PASSES = MT >= 2 ? 2 : 1;
+        constexpr int TPP = MT / PASSES;             // 32-row tiles per pass
+        constexpr int HR = 32 * TPP;                 // rows per pass
         // two waves per slot with two slots, one per slot with four
         static_assert((NS == 2 ? 2 : 1) * HR * RS <= G::SLOT, "epilogue staging must fit the code slots");
         char *region;
@@ -589,10 +596,10 @@ void mx_gemm_tile(GemmArgs p)
         const bool vec_ok = (p.N & 7) == 0 && ncol + 8 <= p.N;
         block_barrier();                             // every wave is done with the code slots
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < PASSES; ++hf) {
 #pragma unroll
-            for (int ii = 0; ii < MT / 2; ++ii) {
-                const int i = hf * (MT / 2) + ii;
+            for (int ii = 0; ii < TPP; ++ii) {
+                const int i = hf * TPP + ii;
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
 #pragma unroll

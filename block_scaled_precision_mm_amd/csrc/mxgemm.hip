@@ -99,7 +99,6 @@ const Variant kVariants[] = {
     MXG_STREAM(2, 2, 4),
     MXG_STREAM(2, 4, 8),
     MXG_STREAM(4, 2, 8),
-    MXG_STREAM(4, 4, 4),
     //          name              MT NW G  KS K4    K8    DMA
     MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048, 1),
     MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048, 1),
@@ -121,6 +120,7 @@ const Variant kVariants[] = {
     MXG_TILE("tile_128x256",     2, 4,  4, 64,   2, 128),
     MXG_TILE("tile_128x128",     2, 2,  2, 128,  2, 128),
     MXG_TILE("tile_128x128_r4",  2, 2,  4, 128,  4, 128),
+    MXG_TILE("tile_64x64_r4",    1, 1,  4, 128,  4, 128),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -352,10 +352,13 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     if (M <= 128 && cdiv(M, 128) * cdiv(N, 128) < 64)
         return find_variant(!is_fp4 || K > 5120 ? "stream_4x2_k8"
                             : K <= 4096 ? "decode_32x64_k2" : "decode_32x64_k2_long");
-    // and 129-256 rows (256 x 4096 x 4096: 12.0 us on stream_4x4_k4 against
-    // 17.3 on tile_128x128 for E2M1, 12.2 against 29.7 for E4M3)
+    // and up to 256 rows with at most 64 such tiles: 64 x 64 tiles with four
+    // code slots (256 x 4096 x 4096: 9.75 us against 12.2 on stream_4x4_k4
+    // and 17.3 on tile_128x128; 256 x 4096 x 14336: 25.9 against 33.3;
+    // E4M3 256 x 4096 x 4096: 14.3 against 15.9; 256 x 4096 x 1024: 5.4
+    // against 6.8)
     if (M <= 256 && cdiv(M, 128) * cdiv(N, 128) <= 64)
-        return find_variant("stream_4x4_k4");
+        return find_variant("tile_64x64_r4");
     // tiles of 256 rows only above 128 rows, where they are not half empty
     // (128 x 25600 x 5120 E2M1: 29.1 us on 128 x 128, 32.7 on 256 x 128);
     // 256 x 256 from 192 tiles (512 x 25600 x 5120: 55.5 us, against 71.8 on
@@ -369,6 +372,14 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant("tile_128x256");
     if (M > 128 && cdiv(M, 256) * cdiv(N, 128) >= 192)
         return find_variant("tile_256x128");
+    // up to 128 tiles of 128 x 128 and K <= 4096: four times the workgroups
+    // on 64 x 64 tiles (512 x 4096 x 4096: 15.2 us against 16.9 on
+    // tile_128x128_r4, E4M3 21.9 against 24.4; 512 x 4096 x 2048: 9.6
+    // against 12.5; E4M3 512 x 2048 x 2048: 8.6 against 18.8; at 160 tiles,
+    // 640 x 4096 x 4096, 20.4 against 17.2, and at K = 14336 the 128 x 128
+    // tile in two K parts is faster)
+    if (cdiv(M, 128) * cdiv(N, 128) <= 128 && K <= 4096)
+        return find_variant("tile_64x64_r4");
     // the 128 x 128 tile's super-stage is little MFMA work: over a long K a
     // ring of four code slots keeps its loads in flight across three of
     // them (128 x 25600 x 5120 E2M1: 32.3 -> 26.6 us; 512 x 4096 x 4096
@@ -392,7 +403,9 @@ struct Config {
 //     18.0 -> 20.2 us);
 //   * 17-32 rows of E2M1 on narrow N (the whole-row decode kernel does not
 //     apply) with K >= 12288: the 32 x 64 stream tile in four K parts
-//     (32 x 4096 x 14336: 14.5 us on stream_2x1_k4 -> 12.7).
+//     (32 x 4096 x 14336: 14.5 us on stream_2x1_k4 -> 12.7);
+//   * 65-128 rows on narrow N that would run the 64 x 128 stream tile: the
+//     64 x 64 four-slot tile in two K parts (below).
 Config pick_config(int is_fp4, int64_t M, int64_t N, int64_t K, bool with_ws)
 {
     Config cf{pick_variant(is_fp4, M, N, K), 1};
@@ -404,6 +417,13 @@ Config pick_config(int is_fp4, int64_t M, int64_t N, int64_t K, bool with_ws)
         return Config{cf.variant, 2};
     if (is_fp4 && M > 16 && M <= 32 && N < 8192 && K >= 12288 && units >= 4)
         return Config{find_variant("stream_2x4_k8"), 4};
+    // 65-128 rows on narrow N where the stream tile would run (E4M3, or
+    // E2M1 with K > 5120): 64 x 64 tiles with four code slots in two K
+    // parts (128 x 4096 x 14336: 22.0 -> 18.1 us; E4M3 128 x 4096 x 8192:
+    // 27.8 -> 18.3; E4M3 128 x 4096 x 4096: 13.9 -> 11.9; whole K on 64 x 64
+    // tiles is no faster than the stream tile at long K)
+    if (cf.variant == find_variant("stream_4x2_k8") && units >= 2)
+        return Config{find_variant("tile_64x64_r4"), 2};
     return cf;
 }
 

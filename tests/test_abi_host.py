@@ -344,12 +344,18 @@ DEFAULTS = [
     (0, 64, 4096, 4096, "stream_2x2_k4"),
     (1, 64, 14336, 4096, "skinny_64x64_k4"),
     (1, 128, 4096, 4096, "decode_32x64_k2"),   # narrow N: too few tiles for the tile kernels
-    (1, 128, 4096, 14336, "stream_4x2_k8"),
+    (1, 128, 4096, 14336, "stream_4x2_k8"),      # whole K (with a workspace: 64 x 64 tiles, 2 parts)
     (0, 128, 4096, 4096, "stream_4x2_k8"),
-    (1, 256, 4096, 4096, "stream_4x4_k4"),
-    (1, 128, 14336, 4096, "tile_128x128_r4"),
+    (1, 256, 4096, 4096, "tile_64x64_r4"),
+    (1, 256, 4096, 1024, "tile_64x64_r4"),
+    (1, 512, 4096, 4096, "tile_64x64_r4"),       # <= 128 tiles of 128 x 128, K <= 4096
+    (0, 512, 2048, 2048, "tile_64x64_r4"),
+    (1, 640, 4096, 4096, "tile_128x128_r4"),     # 160 tiles
+    (1, 512, 4096, 8192, "tile_128x128_r4"),     # long K: 128 x 128 in two parts with a workspace
+    (1, 128, 14336, 4096, "tile_64x64_r4"),      # 112 tiles of 128 x 128
     (1, 128, 25600, 5120, "tile_128x128_r4"),  # no half-empty 256-row tiles; four slots over a long K
-    (1, 333, 517, 1152, "tile_128x128"),       # two slots at short K
+    (1, 333, 517, 1152, "tile_64x64_r4"),      # few tiles
+    (1, 1100, 2048, 1152, "tile_128x128"),     # > 128 tiles, short K: two slots
     (1, 256, 28672, 8192, "tile_128x256"),
     (0, 256, 28672, 8192, "tile_128x256"),
     (1, 8192, 8192, 8192, "tile_256x256"),
@@ -375,7 +381,10 @@ def test_default_variant_choice(lib, is4, M, N, K, name):
 SPLIT_DEFAULTS = [
     # (is_fp4, M, N, K, variant, K parts)
     (1, 512, 4096, 14336, "tile_128x128_r4", 2),
-    (1, 512, 4096, 4096, "tile_128x128_r4", 1),
+    (1, 512, 4096, 4096, "tile_64x64_r4", 1),
+    (1, 128, 4096, 14336, "tile_64x64_r4", 2),
+    (0, 128, 4096, 4096, "tile_64x64_r4", 2),
+    (0, 128, 4096, 8192, "tile_64x64_r4", 2),
     (1, 32, 4096, 14336, "stream_2x4_k8", 4),
     (1, 32, 4096, 4096, "stream_2x1_k4", 1),
     (1, 32, 14336, 4096, "decode_32x64", 1),
