@@ -69,7 +69,7 @@ def parse():
 
 
 KERNEL_HEADER = {"stream_": "mx_stream.hpp", "tile_": "mx_tile.hpp",
-                 "skinny_": "mx_skinny.hpp", "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp",
+                 "decode_": "mx_decode.hpp", "mx_quantize": "mx_quant.hpp",
                  "gstream_": "mx_stream.hpp", "gtile_": "mx_tile.hpp", "fstream_": "mx_stream.hpp",
                  "ftile_": "mx_tile.hpp", "fdecode_": "mx_decode.hpp"}
 

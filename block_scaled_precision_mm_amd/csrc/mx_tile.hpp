@@ -191,11 +191,6 @@ struct TileFrag {
     }
 };
 
-template <int MT, int NT>
-struct TileRegs {
-    u4v a[MT][2], b[NT][2];   // [tile][16-byte half]: E2M1 sub-step h / E4M3 half h
-    unsigned sa[MT], sb[NT];  // 128-K scale dwords of the lane's rows
-};
 
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the

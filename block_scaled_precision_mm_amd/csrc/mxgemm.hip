@@ -20,7 +20,6 @@
 #include "mx_decode.hpp"
 #include "mx_dense.hpp"
 #include "mx_quant.hpp"
-#include "mx_skinny.hpp"
 #include "mx_stream.hpp"
 #include "mx_tile.hpp"
 
@@ -71,16 +70,7 @@ constexpr int ring_depth(int fmt, int mt, int wn)
      {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS, DMA), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS, DMA)},   \
      {K8, K4}, 0, 0}
 
-// Decode-width tiles on the 32x32x64 instruction: waves split K, each
-// streams its run through a private register ring and LDS slot.
-#define MXG_KFN(F, MT, NT, KW, G, O) (&mx_gemm_skinny<F, MT, NT, KW, G, O>)
-#define MXG_KOUTS(F, MT, NT, KW, G) \
-    {MXG_KFN(F, MT, NT, KW, G, OUT_BF16), MXG_KFN(F, MT, NT, KW, G, OUT_F16), MXG_KFN(F, MT, NT, KW, G, OUT_F32)}
-#define MXG_SKINNY(NAME, MT, NT, KW, G)                                             \
-    {NAME, 32 * (MT), 32 * (NT), 64 * (KW),                                         \
-     {MXG_KOUTS(FMT_FP8, MT, NT, KW, G), MXG_KOUTS(FMT_FP4, MT, NT, KW, G)}, {0, 0}, 0, 0}
-
-// Large tiles on the 32x32x64 instruction, loaded straight into LDS: NS
+// Tiles on the 32x32x64 instruction, loaded straight into LDS: NS
 // code slots of SW bytes per row, per format (four slots: three
 // super-stages of prefetch).
 #define MXG_TFN(F, MT, NT, NS, SW, O) (&mx_gemm_tile<F, MT, NT, O, 0, 0, NS, SW>)
@@ -107,7 +97,6 @@ const Variant kVariants[] = {
     MXG_DECODE("decode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048, 0),
     MXG_DECODE("decode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048, 0),
 
-    MXG_SKINNY("skinny_64x64_k4",   2, 2, 4, 4),
 
     // E4M3 on the larger tiles: 64-byte super-stages in four slots (three
     // in flight; 2048 x 4096 x 4096: 61.5 -> 50.5 us, 256 x 28672 x 8192:
@@ -315,11 +304,11 @@ int check_split(const Variant &v, int is_fp4, int64_t M, int64_t N, int64_t K, i
 // Default tile choice, from measured sweeps on MI355X.  Up to 64 rows of A
 // the product is a B stream: for E2M1 with 5-32 rows and wide N the
 // whole-row decode kernel (A and the scales read once per workgroup), else
-// the register-streaming kernel (at 33-64 rows and wide N the split-K skinny
-// tile, which reads A once per workgroup); beyond that the register-staged
-// tile kernels take over, with the largest tile that still gives every
-// compute unit work (per-CU traffic is proportional to tile rows + tile
-// columns, so bigger tiles move fewer bytes per FLOP).
+// the register-streaming kernel (at 33-64 rows and wide N the 64 x 64
+// four-slot tile); beyond that the tile kernels take over, with the largest
+// tile that still gives every compute unit work (per-CU traffic is
+// proportional to tile rows + tile columns, so bigger tiles move fewer bytes
+// per FLOP).
 int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
 {
     // E2M1, 5-32 rows, wide N, A tile fits LDS (K up to 8192 for 16 rows,
@@ -344,8 +333,13 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
     if (M <= 32)
         return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
+    // 33-64 rows on wide N: the 64 x 64 four-slot tile (64 x 14336 x 4096:
+    // 11.7 us against 14.9 on a 64 x 64 split-K tile of register rings,
+    // 64 x 25600 x 5120 24.8 against 32.7, E4M3 48 x 28672 x 4096 29.4
+    // against 40.8); on narrow N the 32 x 32 stream tile (E4M3 64 x 4096 x
+    // 4096: 9.5 us against 14.6 on 64 x 64 tiles, 10.5 with four K parts)
     if (M <= 64)
-        return find_variant(N >= 8192 ? "skinny_64x64_k4" : "stream_2x2_k4");
+        return find_variant(N >= 8192 ? "tile_64x64_r4" : "stream_2x2_k4");
     // 65-128 rows on narrow N give the tile kernels too few output tiles
     // (128 x 4096 x 4096 E2M1: 17.3 us on tile_128x128, 7.9 on the decode
     // kernel; 128 x 4096 x 14336: 56.8 against 21.5 on stream_4x2_k8)

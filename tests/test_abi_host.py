@@ -252,7 +252,7 @@ def test_split_k_configs(lib):
     """Split-K across workgroups: K-part counts, workspace size and errors,
     all decided on the host before any HIP call."""
     tile = _variant(lib, "tile_128x128")
-    skinny = _variant(lib, "skinny_64x64_k4")
+    nosplit = _variant(lib, "decode_32x64_k2")
     M, N, K = 512, 4096, 4096
     args = (A, A, A, A, A, M, N, K, 0)
     # workspace: the fixed region of 16384 counters, then 128 x 2 partial
@@ -275,7 +275,7 @@ def test_split_k_configs(lib):
     assert lib.mx_scaled_mm_config(1, *args, tile, 9, A, 1 << 40, None) == -9      # 4096 / 512 = 8
     assert lib.mx_scaled_mm_config(1, A, A, A, A, A, M, N, 1 << 16, 0, tile, 65, A, 1 << 40, None) == -9
     # a kernel without split-K rejects splits > 1
-    assert lib.mx_scaled_mm_config(1, *args, skinny, 2, A, 1 << 40, None) == -9
+    assert lib.mx_scaled_mm_config(1, *args, nosplit, 2, A, 1 << 40, None) == -9
     # the decode kernels (A tile of the whole K in LDS) take no split-K
     dec = _variant(lib, "decode_32x64")
     assert lib.mx_scaled_mm_config(1, A, A, A, A, A, 32, 14336, 4096, 0, dec, 2, A, 1 << 40, None) == -9
@@ -342,7 +342,8 @@ DEFAULTS = [
     (0, 8, 14336, 4096, "stream_1x2_k4"),
     (1, 32, 4096, 4096, "stream_2x1_k4"),
     (0, 64, 4096, 4096, "stream_2x2_k4"),
-    (1, 64, 14336, 4096, "skinny_64x64_k4"),
+    (1, 64, 14336, 4096, "tile_64x64_r4"),
+    (0, 48, 28672, 4096, "tile_64x64_r4"),
     (1, 128, 4096, 4096, "decode_32x64_k2"),   # narrow N: too few tiles for the tile kernels
     (1, 128, 4096, 14336, "stream_4x2_k8"),      # whole K (with a workspace: 64 x 64 tiles, 2 parts)
     (0, 128, 4096, 4096, "stream_4x2_k8"),
