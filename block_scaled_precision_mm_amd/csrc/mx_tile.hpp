@@ -15,53 +15,58 @@
 // The kernel passes B rows as X and A rows as Y, so lane (r, g) holds
 // C[m0 + r][n0 + 8v + 4g + e]: four runs of four consecutive columns.
 //
-// Super-stages.  The K loop advances SW bytes of every tile row at a time:
-// with SW = 128, 256 K values of E2M1 (four MFMA sub-steps) or 128 of E4M3
-// (two); with SW = 64 half of that.  What decided the width, measured on
-// MI355X at 8192^3 E2M1 with loads alone (every workgroup streaming its
-// 256 + 256 rows from L2): 16-byte loads in which 8 lanes read one row's
-// 128 contiguous bytes move the operands at 25.6 TB/s over the chip,
-// against 15.2 TB/s when 4 lanes read 64 bytes of a row (each L1 request
-// then covers half a cache line, and the number of requests in flight, not
-// bytes, sets the rate); loads straight into LDS stream as fast as loads
-// into registers (26.5 TB/s).  A copy of the loop whose loads touch no
-// memory (out-of-range offsets: same LDS traffic and MFMAs) runs 8192^3 in
-// 189-214 us against 270-298, and 256 x 28672 x 8192 E4M3 in 48 against
-// 97: the super-stage's loads do not land within one super-stage of MFMA
-// work.  Deeper prefetch needs more slots, and LDS holds two 128-byte slots
-// of the largest tiles or four 64-byte ones: E4M3 gains from the latter
-// (2048 x 4096 x 4096 61.5 -> 50.5 us), E2M1 loses (8192^3 +5%: the
-// half-line loads), and the 128 x 128 tile holds four 128-byte slots.
+// Super-stages.  The K loop advances 128 bytes of every tile row at a
+// time: 256 K values of E2M1 (four MFMA sub-steps) or 128 of E4M3 (two).
+// What decided the width, measured on MI355X at 8192^3 E2M1 with loads
+// alone (every workgroup streaming its 256 + 256 rows from L2): 16-byte
+// loads in which 8 lanes read one row's 128 contiguous bytes move the
+// operands at 25.6 TB/s over the chip, against 15.2 TB/s when 4 lanes read
+// 64 bytes of a row (each L1 request then covers half a cache line, and the
+// number of requests in flight, not bytes, sets the rate); loads straight
+// into LDS stream as fast as loads into registers (26.5 TB/s).  A copy of
+// the loop whose loads touch no memory (out-of-range offsets: same LDS
+// traffic and MFMAs) ran 8192^3 in 189-214 us against 270-298, and
+// 256 x 28672 x 8192 E4M3 in 48 against 97: a super-stage's loads did not
+// land within one super-stage of MFMA work.  LDS holds two 128-byte slots
+// of the larger tiles; four 64-byte slots (three super-stages in flight)
+// helped E4M3 and cost E2M1 5% at 8192^3 (the half-line loads), and were
+// overtaken on every shape by two 128-byte slots with the split barrier
+// below (E4M3 2048 x 4096 x 4096: 50.5 -> 41.0 us, 8192^3: 468 -> 437).
 //
 // Data path.  Global -> LDS directly (gfx950's 16-byte buffer load to LDS:
 // no staging registers, no LDS store instructions).  A load instruction
-// fills 1 KB of LDS in lane order: 8 rows x 128 bytes (SW = 128) or 16 rows
-// x 64 bytes, lane l at 16*l, so lane l (row l/LPR of its block, position
-// p = l%LPR, LPR = SW/16 lanes per row) fetches the row's chunk
-// c = p ^ s(row): the lanes of a row still read its SW contiguous bytes,
-// and chunk c of row `row` sits at SW*row + 16*(c ^ s(row)).  With
-// s(row) = (row >> 1) & 7 (SW = 128) or (row >> 2) & 3 (SW = 64), a
-// fragment read (16 consecutive lanes = 16 consecutive rows, one chunk)
-// touches 16 different 16-byte bank groups of the 256 bytes the LDS banks
-// cover.  Scale codes: 16 bytes per row per period of four 128-K steps,
-// through registers, stored transposed ([step][row] dwords), so an MFMA's
-// scale operand is one dword read plus a shift; the two sub-steps of a
-// 128-K step share the dword (read once).  The code slots and the scale
-// buffers are separate LDS objects, so the compiler can tell a fragment
-// read of one slot from the loads still landing in another.
+// fills 1 KB of LDS in lane order: 8 rows x 128 bytes, lane l at 16*l, so
+// lane l (row l/8 of its block, position p = l%8) fetches the row's chunk
+// c = p ^ s(row): the lanes of a row still read its 128 contiguous bytes,
+// and chunk c of row `row` sits at 128*row + 16*(c ^ s(row)).  With
+// s(row) = (row >> 1) & 7, a fragment read (16 consecutive lanes = 16
+// consecutive rows, one chunk) touches 16 different 16-byte bank groups of
+// the 256 bytes the LDS banks cover.  Scale codes: 16 bytes per row per
+// period of four 128-K steps, through registers, stored transposed
+// ([step][row] dwords), so an MFMA's scale operand is one dword read plus a
+// shift; the two sub-steps of a 128-K step share the dword (read once).
+// The code slots and the scale buffers are separate LDS objects, so the
+// compiler can tell a fragment read of one slot from the loads still
+// landing in another.
 //
 // Pipeline (iteration u computes super-stage u; NS = 2 or 4 code slots).
-// Sub-step h's fragments are read while sub-step h-1's MFMAs run.  Before
-// the last sub-step: wait for super-stage u+1's loads, barrier (every
-// wave's loads of u+1 have landed and every wave is done reading slot u),
-// issue the loads of u+NS into slot u, and at a period start write the next
-// period's scale codes and load the one after; the last sub-step's MFMAs
-// then cover the read of super-stage u+1's first fragments.  A load has
-// NS-1 iterations to land: four slots where a super-stage is little MFMA
-// work (the 128 x 128 tile: 16 MFMAs per wave, less than an HBM round
-// trip) and LDS allows.  The loop runs whole periods; super-stages past K
-// (and rows past M or N) load zero codes through out-of-range offsets and
-// have zero scale codes, and add exactly +0.
+// Sub-step h's fragments are read while sub-step h-1's MFMAs run, so by the
+// last sub-step every fragment of slot u is in registers.  Two slots: at
+// the last sub-step a barrier (every wave is done reading slot u), the
+// loads of u+2 into slot u and at a period start the next period's scale
+// codes written, under the first half of its MFMAs; then wait for
+// super-stage u+1's loads, a second barrier (every wave's have landed),
+// the scale loads of a later period, and super-stage u+1's first fragments
+// read under the second half.  Issuing u+2's loads before waiting for u+1
+// keeps a late super-stage from also delaying the next one's loads: with
+// load latency L above the compute time T of an iteration, a loop that
+// waits first runs at L per iteration, this one at (L + T) / 2
+// (256 x 28672 x 8192: E2M1 55.5 -> 49.6 us, E4M3 91.5 -> 80.5).  Four
+// slots (where a super-stage is little MFMA work and LDS allows: the
+// 128 x 128 and 64 x 64 tiles): wait for u+1, one barrier, loads of u+4;
+// a load has three iterations to land.  The loop runs whole periods;
+// super-stages past K (and rows past M or N) load zero codes through
+// out-of-range offsets and have zero scale codes, and add exactly +0.
 //
 // Waves.  Four waves in 2 x 2, each owning a (32*MT) x (32*NT) part of the
 // (64*MT) x (64*NT) workgroup tile; at MT = NT = 4 the 256 accumulator
@@ -86,11 +91,11 @@
 
 namespace mxg {
 
-template <int F, int MT, int NT, int NS = 2, int SW_ = 128>
+template <int F, int MT, int NT, int NS = 2>
 struct TileGeom {
     static constexpr int BM = 64 * MT, BN = 64 * NT;    // workgroup tile
     static constexpr int ROWS = BM + BN;                 // A rows then B rows
-    static constexpr int SW = SW_;                       // row bytes per super-stage (128 or 64)
+    static constexpr int SW = 128;                       // row bytes per super-stage
     static constexpr int KSS = SW * (F == FMT_FP4 ? 2 : 1);   // K values per super-stage
     static constexpr int SUB = KSS / 64;                 // 32x32x64 sub-steps per super-stage
     static constexpr int SLOT = ROWS * SW;               // one code slot (unpadded, swizzled)
@@ -118,7 +123,6 @@ struct TileGeom {
         return per % NS == 0 ? per : (NS % per == 0 ? NS : per * NS);
     }();
     static_assert(NS == 2 || NS == 4, "two or four code slots");
-    static_assert(SW == 128 || SW == 64, "super-stages of 64 or 128 bytes per row");
     static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
     static_assert((ROWS / RPL) % 4 == 0, "load blocks must spread evenly over 4 waves");
     static_assert(BM % RPL == 0, "A and B rows never share a load block");
@@ -126,14 +130,8 @@ struct TileGeom {
     // byte offset of 16-byte chunk c of tile row `row` in a code slot: the
     // chunk's place XORed with the row so that the 16 rows of a fragment
     // read fall on 16 different 16-byte bank groups
-    __device__ static constexpr int code_off(int row, int c)
-    {
-        if constexpr (SW == 128)
-            return row * 128 + 16 * (c ^ ((row >> 1) & 7));
-        else
-            return row * 64 + 16 * (c ^ ((row >> 2) & 3));
-    }
-    __device__ static constexpr int swz(int row) { return SW == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
+    __device__ static constexpr int swz(int row) { return (row >> 1) & 7; }
+    __device__ static constexpr int code_off(int row, int c) { return row * SW + 16 * (c ^ swz(row)); }
 };
 
 // Linear workgroup index -> position in tile order: workgroups b, b + 8,
@@ -195,12 +193,12 @@ struct TileFrag {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2, int SW = 128>
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
     static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
-    using G = TileGeom<F, MT, NT, NS, SW>;
+    using G = TileGeom<F, MT, NT, NS>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     // The two code slots and the scale buffers are separate LDS objects: the
     // compiler then knows that a fragment read of one slot cannot touch what
@@ -379,7 +377,8 @@ void mx_gemm_tile(GemmArgs p)
                 acc[i][j][e] = 0.f;
 
     // the half of a 128-K step: blocks 2*half + g of the step's scale dword
-    auto compute = [&](const Frag &R, int half) {
+    // MFMAs lo .. hi-1 of the sub-step, in (i, j) order
+    auto compute = [&](const Frag &R, int half, auto lo, auto hi) {
         const unsigned sh = 8u * (2 * half + g);
         unsigned xs[NT], ys[MT];
 #pragma unroll
@@ -387,9 +386,8 @@ void mx_gemm_tile(GemmArgs p)
 #pragma unroll
         for (int i = 0; i < MT; ++i) ys[i] = R.sa[i] >> sh;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
+        for (int ij = decltype(lo)::value; ij < decltype(hi)::value; ++ij) {
+                const int i = ij / NT, j = ij % NT;
                 v8i x, y;
                 if constexpr (F == FMT_FP4) {
                     const u4v bx = R.b[j][0], ay = R.a[i][0];
@@ -401,7 +399,7 @@ void mx_gemm_tile(GemmArgs p)
                     y = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 }
                 acc[i][j] = mfma32<F>(x, xs[j], y, ys[i], acc[i][j]);
-            }
+        }
     };
 
     constexpr int NM = MT * NT;                  // MFMAs per sub-step
@@ -416,38 +414,30 @@ void mx_gemm_tile(GemmArgs p)
     scale_load(set_0{}, 0);
     wait_vm<0>();
     scale_write(set_0{}, 0);
-    if constexpr (NS == 2) {
-        code_load(slot_0{}, 0);
-        code_load(std::integral_constant<int, 1>{}, 1);
-        scale_load(std::integral_constant<int, 1 % SSETS>{}, 1);
-        wait_vm<G::LB + G::LS>();      // super-stage 0 has landed
-    } else {
-        // the staging loads first: the loop then starts, as it continues,
-        // with code loads as the most recent ones (the compiler's own wait
-        // bookkeeping merges the two at the loop head)
-        static_for<SLEAD - 1>([&](auto pc) {
-            constexpr int q = 1 + decltype(pc)::value;
-            scale_load(std::integral_constant<int, q % SSETS>{}, q);
-        });
-        __builtin_amdgcn_sched_barrier(0);   // (the scheduler keeps that order)
-        static_for<NS>([&](auto sc) { code_load(sc, decltype(sc)::value); });
-        wait_vm_known<(NS - 1) * G::LB>();   // super-stage 0 has landed
-    }
+    // the staging loads first: the loop then starts, as it continues, with
+    // code loads as the most recent ones (the compiler's own wait
+    // bookkeeping merges the two at the loop head)
+    static_for<SLEAD - 1>([&](auto pc) {
+        constexpr int q = 1 + decltype(pc)::value;
+        scale_load(std::integral_constant<int, q % SSETS>{}, q);
+    });
+    __builtin_amdgcn_sched_barrier(0);   // (the scheduler keeps that order)
+    static_for<NS>([&](auto sc) { code_load(sc, decltype(sc)::value); });
+    wait_vm_known<(NS - 1) * G::LB>();   // super-stage 0 has landed
     block_barrier();
     read(R[0], slot_0{}, 0, kk_0{}, nullptr);
 
     // Iteration u: sub-steps 0 .. SUB-2 read the next sub-step while
-    // computing; before the last one, wait for super-stage u+1, barrier,
-    // refill slot u with super-stage u+NS and at a period start write the
-    // next period's scale codes and stage a later one; the last sub-step
-    // reads super-stage u+1's first fragments.
+    // computing; the last one refills slot u with super-stage u+NS, at a
+    // period start writes the next period's scale codes and stages a later
+    // one, and reads super-stage u+1's first fragments (see "Pipeline").
     auto iteration = [&](auto uc, int u) {
         constexpr int i = decltype(uc)::value;   // u % TURN
         constexpr int pu = i % G::P;             // u % P
         using mine = std::integral_constant<int, i % NS>;         // slot of u and u + NS
         using next = std::integral_constant<int, (i + 1) % NS>;   // slot of u + 1
-        // loads issued after super-stage u+1's, which may stay in flight
-        // while it is waited for: the code loads of u+2 .. u+NS-1 and the
+        // Four slots: loads issued after super-stage u+1's, which may stay
+        // in flight while it is waited for: the code loads of u+2 .. u+NS-1 and the
         // scale loads issued with those (iterations u+2-NS .. u-1 that start
         // a period).  Not counted, since counting too few only waits longer
         // while counting one too many races with a load still landing: the
@@ -468,17 +458,53 @@ void mx_gemm_tile(GemmArgs p)
             constexpr int fb = (i * G::SUB + h) & 1;         // its fragment buffer
             __builtin_amdgcn_sched_barrier(0);
             constexpr int kn = h == G::SUB - 1 ? (pu + 1) % G::P * G::SUB : kk + 1;   // the next one's
+            using wset = std::integral_constant<int, (i / G::P + 1) % SSETS>;
+            using lset = std::integral_constant<int, (i / G::P + SLEAD) % SSETS>;
+            using c0 = std::integral_constant<int, 0>;
+            using cN = std::integral_constant<int, NM>;
+            if constexpr (NS == 2 && h == G::SUB - 1) {
+                // two slots: slot u refilled as soon as every wave has read
+                // it, super-stage u+1 waited for after that
+                using cH = std::integral_constant<int, NM / 2>;
+                block_barrier();
+                if constexpr (pu == 0)
+                    scale_write(wset{}, u / G::P + 1);
+                code_load(mine{}, u + NS);
+                compute(R[fb], kk % 2, c0{}, cH{});
+                constexpr int NM1 = NM / 2, NMEM1 = G::LB + (pu == 0 ? 4 * G::LS : 0);
+                static_for<NM1>([&](auto kc) {
+                    constexpr int K = decltype(kc)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    constexpr int m0 = NMEM1 * K / NM1, m1 = NMEM1 * (K + 1) / NM1;
+                    if constexpr (m1 > m0)
+                        __builtin_amdgcn_sched_group_barrier(0x020 | 0x200, m1 - m0, 0);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_known<G::LB>();   // super-stage u+1 has landed; u+2's loads may not have
+                block_barrier();
+                if constexpr (pu == 0)
+                    scale_load(lset{}, u / G::P + SLEAD);
+                read(R[fb ^ 1], next{}, u + 1, std::integral_constant<int, kn>{}, &R[fb]);
+                compute(R[fb], kk % 2, cH{}, cN{});
+                constexpr int NM2 = NM - NM1, NRD2 = NCR + (kn % 2 == 0 ? MT + NT : 0);
+                static_for<NM2>([&](auto kc) {
+                    constexpr int K = decltype(kc)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    constexpr int r0 = NRD2 * K / NM2, r1 = NRD2 * (K + 1) / NM2;
+                    if constexpr (r1 > r0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, r1 - r0, 0);
+                    if constexpr (pu == 0 && K < G::LS)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                return;
+            }
             if constexpr (h == G::SUB - 1) {
                 // super-stage u+1 (and any scale loads issued before it) has landed
-                if constexpr (NS == 2)
-                    wait_vm<AFTER>();
-                else
-                    wait_vm_known<AFTER>();
+                wait_vm_known<AFTER>();
                 block_barrier();
                 // the period of u is u0 / P + i / P with u0 / P a multiple of
                 // SSETS, so the staging set of any period is known here
-                using wset = std::integral_constant<int, (i / G::P + 1) % SSETS>;
-                using lset = std::integral_constant<int, (i / G::P + SLEAD) % SSETS>;
                 if constexpr (pu == 0)
                     scale_write(wset{}, u / G::P + 1);
                 code_load(mine{}, u + NS);
@@ -488,7 +514,7 @@ void mx_gemm_tile(GemmArgs p)
             } else {
                 read(R[fb ^ 1], mine{}, u, std::integral_constant<int, kn>{}, &R[fb]);
             }
-            compute(R[fb], kk % 2);
+            compute(R[fb], kk % 2, c0{}, cN{});
             // interleave: each MFMA followed by its share of the memory
             // operations (loads and scale writes at the last sub-step)
             constexpr int NMEM = h == G::SUB - 1 ? G::LB + (pu == 0 ? 5 * G::LS : 0) : 0;

@@ -70,16 +70,14 @@ constexpr int ring_depth(int fmt, int mt, int wn)
      {MXG_DOUTS(FMT_FP8, MT, NW, K8, G, KS, DMA), MXG_DOUTS(FMT_FP4, MT, NW, K4, G, KS, DMA)},   \
      {K8, K4}, 0, 0}
 
-// Tiles on the 32x32x64 instruction, loaded straight into LDS: NS
-// code slots of SW bytes per row, per format (four slots: three
-// super-stages of prefetch).
-#define MXG_TFN(F, MT, NT, NS, SW, O) (&mx_gemm_tile<F, MT, NT, O, 0, 0, NS, SW>)
-#define MXG_TOUTS(F, MT, NT, NS, SW)                                                                \
-    {MXG_TFN(F, MT, NT, NS, SW, OUT_BF16), MXG_TFN(F, MT, NT, NS, SW, OUT_F16),                     \
-     MXG_TFN(F, MT, NT, NS, SW, OUT_F32)}
-#define MXG_TILE(NAME, MT, NT, NS8, SW8, NS4, SW4)                                                  \
-    {NAME, 64 * (MT), 64 * (NT), 256,                                                               \
-     {MXG_TOUTS(FMT_FP8, MT, NT, NS8, SW8), MXG_TOUTS(FMT_FP4, MT, NT, NS4, SW4)}, {0, 0}, 1, 1}
+// Tiles on the 32x32x64 instruction, loaded straight into LDS: NS code
+// slots of 128 bytes per row (four slots: three super-stages of prefetch).
+#define MXG_TFN(F, MT, NT, NS, O) (&mx_gemm_tile<F, MT, NT, O, 0, 0, NS>)
+#define MXG_TOUTS(F, MT, NT, NS) \
+    {MXG_TFN(F, MT, NT, NS, OUT_BF16), MXG_TFN(F, MT, NT, NS, OUT_F16), MXG_TFN(F, MT, NT, NS, OUT_F32)}
+#define MXG_TILE(NAME, MT, NT, NS)          \
+    {NAME, 64 * (MT), 64 * (NT), 256,       \
+     {MXG_TOUTS(FMT_FP8, MT, NT, NS), MXG_TOUTS(FMT_FP4, MT, NT, NS)}, {0, 0}, 1, 1}
 
 const Variant kVariants[] = {
     MXG_STREAM(1, 1, 4),
@@ -96,20 +94,13 @@ const Variant kVariants[] = {
     // the same with room for a longer A tile (more LDS: 1-2% slower at K <= 4096)
     MXG_DECODE("decode_32x64_k2_long", 2, 4, 2, 2, 5120, 2048, 0),
     MXG_DECODE("decode_16x64_k2_long", 1, 4, 2, 2, 8192, 2048, 0),
-
-
-    // E4M3 on the larger tiles: 64-byte super-stages in four slots (three
-    // in flight; 2048 x 4096 x 4096: 61.5 -> 50.5 us, 256 x 28672 x 8192:
-    // 96 -> 92); E2M1 keeps 128-byte super-stages in two (8192^3: 270-275
-    // against 284-298 us with 64-byte stages, whose half-line loads cost the
-    // address unit more than the deeper prefetch gains)
-    //        name               MT NT  E4M3     E2M1
-    MXG_TILE("tile_256x256",     4, 4,  4, 64,   2, 128),
-    MXG_TILE("tile_256x128",     4, 2,  4, 64,   2, 128),
-    MXG_TILE("tile_128x256",     2, 4,  4, 64,   2, 128),
-    MXG_TILE("tile_128x128",     2, 2,  2, 128,  2, 128),
-    MXG_TILE("tile_128x128_r4",  2, 2,  4, 128,  4, 128),
-    MXG_TILE("tile_64x64_r4",    1, 1,  4, 128,  4, 128),
+    //        name               MT NT NS
+    MXG_TILE("tile_256x256",     4, 4, 2),
+    MXG_TILE("tile_256x128",     4, 2, 2),
+    MXG_TILE("tile_128x256",     2, 4, 2),
+    MXG_TILE("tile_128x128",     2, 2, 2),
+    MXG_TILE("tile_128x128_r4",  2, 2, 4),
+    MXG_TILE("tile_64x64_r4",    1, 1, 4),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -257,25 +257,25 @@ def test_deterministic(mx):
         mxcheck.check_f32(x1, cref, S, K, None, mx.mx_variant_name(v))
 
 
-# The tile variants that keep several super-stages of loads in flight (four
-# code slots: the E4M3 instantiations of the larger tiles and the *_r4
-# tiles) wait for a super-stage with a count of the loads issued after it;
-# a count one too high races with the loads still landing.  Each is run
+# Every tile variant waits for a super-stage with a count of the loads
+# issued after it (two slots: the next super-stage's loads, issued before
+# the wait; four slots: those of the two after it and their scale loads); a
+# count one too high races with the loads still landing.  Each is run
 # repeatedly on ragged shapes whose K spans several periods (and a tail),
 # every run bit-identical and within the bound.
-FOUR_SLOT = ["tile_256x256", "tile_256x128", "tile_128x256", "tile_128x128_r4", "tile_64x64_r4"]
+TILES = ["tile_256x256", "tile_256x128", "tile_128x256", "tile_128x128", "tile_128x128_r4", "tile_64x64_r4"]
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
 @pytest.mark.parametrize("shape", [(33, 200, 640), (100, 130, 1152), (70, 300, 2688)],
                          ids=lambda s: "%dx%dx%d" % s)
-def test_four_slot_variants_repeat(mx, fmt, shape):
+def test_tile_variants_repeat(mx, fmt, shape):
     M, N, K = shape
     a, b, sa, sb = quantized(fmt, M, N, K, seed=M * 17 + N + K)
     cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
     model = e4m3_model(fmt, a, b, sa, sb, M, N, K)
     print("case", fmt, shape, flush=True)
-    for name in FOUR_SLOT:
+    for name in TILES:
         v = next(i for i in range(mx.mx_num_variants()) if mx.mx_variant_name(i) == name)
         first = run(mx, fmt, a, b, sa, sb, M, N, K, "f32", v)
         mxcheck.check_f32(first, cref, S, K, model, "%s %s %s" % (fmt, shape, name))
