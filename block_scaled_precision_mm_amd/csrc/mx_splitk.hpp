@@ -114,19 +114,17 @@ __device__ __forceinline__ bool splitk_reduce(const GemmArgs &p, int tile, int t
     __syncthreads();
     if (arrived != (unsigned)(S - 1))
         return false;
-    // the last part: sum in part order, its own part from its registers
+    // the last part: sum in part order, every part (its own too, stored
+    // above) read back, so no piece is needed in registers past its store
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const v4f own = get(j);
-        v4f sum = own;
+        v4f sum;
         for (int q = 0; q < S; ++q) {
-            v4f v = own;
-            if (q != part) {
-                const float *src = slots + (size_t)q * FL + 4 * j * NTHR + tid;
+            const float *src = slots + (size_t)q * FL + 4 * j * NTHR + tid;
+            v4f v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = __hip_atomic_load(src + e * NTHR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int e = 0; e < 4; ++e)
+                v[e] = __hip_atomic_load(src + e * NTHR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sum = q == 0 ? v : sum + v;
         }
         set(j, sum);

@@ -126,7 +126,7 @@ struct TileGeom {
     static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
     static_assert((ROWS / RPL) % 4 == 0, "load blocks must spread evenly over 4 waves");
     static_assert(BM % RPL == 0, "A and B rows never share a load block");
-    static_assert((NS - 1) * LB + 2 * LS < 64, "outstanding loads must fit the vmcnt field");
+    static_assert(NS * LB + SLEAD * LS < 64, "outstanding loads must fit the vmcnt field");
     // byte offset of 16-byte chunk c of tile row `row` in a code slot: the
     // chunk's place XORed with the row so that the 16 rows of a fragment
     // read fall on 16 different 16-byte bank groups
@@ -299,7 +299,7 @@ void mx_gemm_tile(GemmArgs p)
     // [A rows | B rows]; lane l holds row l's 16 bytes of the period
     // staging registers of a period's codes (G::SSETS sets, see TileGeom)
     constexpr int SSETS = G::SSETS, SLEAD = G::SLEAD;
-    u4v sstg[SSETS][G::LS];
+    u4v sstg[SSETS + 1][G::LS];   // (set SSETS: period 0, in the prologue)
     auto scale_load = [&](auto set, int period) {   // set = period % SSETS
         const bool live = period * G::P < U;
 #pragma unroll
@@ -408,21 +408,21 @@ void mx_gemm_tile(GemmArgs p)
 
     // prologue: period 0's scale codes written, the next staged;
     // super-stages 0 .. NS-1 requested; super-stage 0's first fragments read
-    using set_0 = std::integral_constant<int, 0>;
     using slot_0 = std::integral_constant<int, 0>;
     using kk_0 = std::integral_constant<int, 0>;
-    scale_load(set_0{}, 0);
-    wait_vm<0>();
-    scale_write(set_0{}, 0);
-    // the staging loads first: the loop then starts, as it continues, with
-    // code loads as the most recent ones (the compiler's own wait
-    // bookkeeping merges the two at the loop head)
+    // All requested before any is waited for (one memory latency, not
+    // two).  The staging loads first: the loop then starts, as it
+    // continues, with code loads as the most recent ones (the compiler's
+    // own wait bookkeeping merges the two at the loop head).
+    using set_p0 = std::integral_constant<int, SSETS>;
+    scale_load(set_p0{}, 0);
     static_for<SLEAD - 1>([&](auto pc) {
         constexpr int q = 1 + decltype(pc)::value;
         scale_load(std::integral_constant<int, q % SSETS>{}, q);
     });
     __builtin_amdgcn_sched_barrier(0);   // (the scheduler keeps that order)
     static_for<NS>([&](auto sc) { code_load(sc, decltype(sc)::value); });
+    scale_write(set_p0{}, 0);            // (the compiler waits for its registers)
     wait_vm_known<(NS - 1) * G::LB>();   // super-stage 0 has landed
     block_barrier();
     read(R[0], slot_0{}, 0, kk_0{}, nullptr);
