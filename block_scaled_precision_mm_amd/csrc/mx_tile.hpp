@@ -169,11 +169,12 @@ __device__ __forceinline__ void static_for(Fn &&f)
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int F>
+// SEL: the byte of each scale register that holds the lane's code
+template <int F, int SEL = 0>
 __device__ __forceinline__ v16f mfma32(v8i x, unsigned sx, v8i y, unsigned sy, v16f acc)
 {
     constexpr int c = FmtTraits<F>::mfma_code;
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, c, c, 0, (int)sx, 0, (int)sy);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, c, c, SEL, (int)sx, SEL, (int)sy);
 }
 
 // One sub-step's fragments of a wave's tile: the lane's 16 (E2M1) or 32
@@ -341,21 +342,28 @@ void mx_gemm_tile(GemmArgs p)
     };
 
     // ---- fragments of one sub-step: lane (r, g) reads rows wm*32*MT + 32i
-    // + r (A) and wn*32*NT + 32j + r (B); E2M1 sub-step h of a super-stage
-    // is chunk 2h + g, E4M3 sub-step h chunks 4h + g and 4h + 2 + g.  kk is
-    // the sub-step's 64-K index within its period: its scale dword is that
-    // of 128-K step kk / 2.
+    // + r (A) and wn*32*NT + 32j + r (B).  kk is the sub-step's 64-K index
+    // within its period.  E4M3 sub-step h of a super-stage is chunks 4h + g
+    // and 4h + 2 + g, and its scale dword is that of 128-K step kk / 2.
+    // E2M1 sub-step h takes K-block h of each of the super-stage's two
+    // 128-K steps, lane half g step g (chunk h + 4g): the products of a
+    // super-stage are summed in another order, and a lane uses one scale
+    // dword (its step's) for all four sub-steps, byte h selected by the
+    // instruction.
     constexpr int NV = FmtTraits<F>::nvec;
     using Frag = TileFrag<F, MT, NT>;
+    // whether sub-step kk reads scale dwords (else it reuses the previous one's)
+    constexpr auto new_scales = [](int kk) { return F == FMT_FP4 ? kk % G::SUB == 0 : kk % 2 == 0; };
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
     auto read = [&](Frag &R, auto k, int u, auto kkc, const Frag *prev) {
         constexpr int kk = decltype(kkc)::value;
         constexpr int h = kk % G::SUB;
         const char *slot = slot_of(k);
-        const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + (kk / 2) * G::SROWS * 4;
+        const int step = F == FMT_FP4 ? kk / G::SUB * 2 + g : kk / 2;   // of the scale dword
+        const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + step * G::SROWS * 4;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int c = F == FMT_FP4 ? 2 * h + g : 4 * h + 2 * v + g;
+            const int c = F == FMT_FP4 ? h + 4 * g : 4 * h + 2 * v + g;
 #pragma unroll
             for (int i = 0; i < MT; ++i)
                 R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
@@ -363,9 +371,9 @@ void mx_gemm_tile(GemmArgs p)
             for (int j = 0; j < NT; ++j)
                 R.b[j][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(brow + 32 * j, c));
         }
-        // the two sub-steps of a 128-K step share its scale dword: an odd
-        // sub-step takes it from the even one's registers
-        if constexpr (kk % 2 == 1) {
+        // sub-steps that share a scale dword take it from the first one's
+        // registers
+        if constexpr (!new_scales(kk)) {
             R.sa_from(*prev);
             return;
         }
@@ -387,9 +395,12 @@ void mx_gemm_tile(GemmArgs p)
                 acc[i][j][e] = 0.f;
 
     // the half of a 128-K step: blocks 2*half + g of the step's scale dword
-    // MFMAs lo .. hi-1 of the sub-step, in (i, j) order
-    auto compute = [&](const Frag &R, int half, auto lo, auto hi) {
-        const unsigned sh = 8u * (2 * half + g);
+    // MFMAs lo .. hi-1 of sub-step kk, in (i, j) order; the scale byte
+    // of sub-step kk: E2M1 byte kk % SUB of the lane's dword, E4M3 byte
+    // 2 * (kk % 2) + g (shifted down to byte 0)
+    auto compute = [&](const Frag &R, auto kkc, auto lo, auto hi) {
+        constexpr int kk = decltype(kkc)::value;
+        const unsigned sh = F == FMT_FP4 ? 0u : 8u * (2 * (kk % 2) + g);
         unsigned xs[NT], ys[MT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) xs[j] = R.sb[j] >> sh;
@@ -408,7 +419,7 @@ void mx_gemm_tile(GemmArgs p)
                     x = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
                     y = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 }
-                acc[i][j] = mfma32<F>(x, xs[j], y, ys[i], acc[i][j]);
+                acc[i][j] = mfma32<F, F == FMT_FP4 ? kk % G::SUB : 0>(x, xs[j], y, ys[i], acc[i][j]);
         }
     };
 
@@ -480,7 +491,7 @@ void mx_gemm_tile(GemmArgs p)
                 if constexpr (pu == 0)
                     scale_write(wset{}, u / G::P + 1);
                 code_load(mine{}, u + NS);
-                compute(R[fb], kk % 2, c0{}, cH{});
+                compute(R[fb], std::integral_constant<int, kk>{}, c0{}, cH{});
                 constexpr int NM1 = NM / 2, NMEM1 = G::LB + (pu == 0 ? 4 * G::LS : 0);
                 static_for<NM1>([&](auto kc) {
                     constexpr int K = decltype(kc)::value;
@@ -495,8 +506,8 @@ void mx_gemm_tile(GemmArgs p)
                 if constexpr (pu == 0)
                     scale_load(lset{}, u / G::P + SLEAD);
                 read(R[fb ^ 1], next{}, u + 1, std::integral_constant<int, kn>{}, &R[fb]);
-                compute(R[fb], kk % 2, cH{}, cN{});
-                constexpr int NM2 = NM - NM1, NRD2 = NCR + (kn % 2 == 0 ? MT + NT : 0);
+                compute(R[fb], std::integral_constant<int, kk>{}, cH{}, cN{});
+                constexpr int NM2 = NM - NM1, NRD2 = NCR + (new_scales(kn) ? MT + NT : 0);
                 static_for<NM2>([&](auto kc) {
                     constexpr int K = decltype(kc)::value;
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -524,11 +535,11 @@ void mx_gemm_tile(GemmArgs p)
             } else {
                 read(R[fb ^ 1], mine{}, u, std::integral_constant<int, kn>{}, &R[fb]);
             }
-            compute(R[fb], kk % 2, c0{}, cN{});
+            compute(R[fb], std::integral_constant<int, kk>{}, c0{}, cN{});
             // interleave: each MFMA followed by its share of the memory
             // operations (loads and scale writes at the last sub-step)
             constexpr int NMEM = h == G::SUB - 1 ? G::LB + (pu == 0 ? 5 * G::LS : 0) : 0;
-            constexpr int NRD = NCR + (kn % 2 == 0 ? MT + NT : 0);
+            constexpr int NRD = NCR + (new_scales(kn) ? MT + NT : 0);
             static_for<NM>([&](auto kc) {
                 constexpr int K = decltype(kc)::value;
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
