@@ -10,17 +10,19 @@
 //     workspace the caller provides (part s of tile t), in the thread layout
 //     it holds it in (so the write is coalesced and no workgroup needs
 //     another's layout);
-//   * those stores, the tile's arrival counter and the reads below are
-//     device-scope accesses (coherent across MI355X's XCDs, whose L2s are
-//     not coherent with each other for ordinary accesses) -- no fence, so
-//     no workgroup writes back or invalidates a whole L2, which made the
-//     first version of this scheme ten times slower than no split at all;
-//     each thread waits for its stores to complete before the workgroup
-//     bumps the counter with a device-scope atomic add;
+//   * those stores and the reads below carry the cache policy of
+//     device-scope accesses (write through / read past the XCD's L2:
+//     MI355X's eight L2s are not coherent with each other for ordinary
+//     accesses), 16 bytes per thread each, and the tile's arrival counter
+//     is a device-scope atomic -- no fence, so no workgroup writes back or
+//     invalidates a whole L2, which made the first version of this scheme
+//     ten times slower than no split at all (dword-sized accesses cost the
+//     last workgroup of a tile another factor of two to four at eight
+//     parts); each thread waits for its stores to complete before the
+//     workgroup bumps the counter;
 //   * the workgroup that sees S-1 arrivals before its own is the last: it
-//     adds the S parts in part order 0, 1, .., S-1 (the others' read back
-//     from their slots, its own from its registers at its place in that
-//     order), so the sequence of FP32 additions is the same whoever
+//     reads the S parts back (its own too) and adds them in part order
+//     0, 1, .., S-1, so the sequence of FP32 additions is the same whoever
 //     arrives last; it resets the counter to zero for the next call on the
 //     same workspace, and stores the sum through the kernel's normal
 //     epilogue.  The others exit.  No workgroup ever waits for another.
@@ -92,19 +94,16 @@ template <int NV, int NTHR, class Get, class Set>
 __device__ __forceinline__ bool splitk_reduce(const GemmArgs &p, int tile, int tid, Get &&get, Set &&set)
 {
     constexpr int FL = NV * NTHR * 4;   // floats per partial tile
+    constexpr int DEV = 16;             // cache policy of a device-scope access
     __shared__ unsigned arrived;
     const int S = p.splits, part = (int)blockIdx.z;
-    float *slots = p.ws + (size_t)tile * S * FL;
-    // slot layout [piece j][float e][thread]: every store and load below
-    // moves 256 contiguous bytes per wave
-    float *mine = slots + (size_t)part * FL;
+    // slot layout [part][piece j][thread][4 floats]: every access below
+    // moves 16 contiguous bytes per thread, 1 KB per wave
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ws + (size_t)tile * S * FL, (unsigned)(S * FL * 4));
+    auto at = [&](int q, int j) { return (unsigned)(((q * NV + j) * NTHR + tid) * 16); };
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const v4f v = get(j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            __hip_atomic_store(mine + (4 * j + e) * NTHR + tid, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int j = 0; j < NV; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, get(j)), rs, at(part, j), 0, DEV);
     // this thread's stores have completed (device-wide visible) before the
     // workgroup's arrival is counted
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -114,20 +113,27 @@ __device__ __forceinline__ bool splitk_reduce(const GemmArgs &p, int tile, int t
     __syncthreads();
     if (arrived != (unsigned)(S - 1))
         return false;
-    // the last part: sum in part order, every part (its own too, stored
-    // above) read back, so no piece is needed in registers past its store
+    // the last part: sum in part order, JG pieces at a time (their loads
+    // in flight together)
+    constexpr int JG = NV < 8 ? NV : 8;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        v4f sum;
+    for (int j0 = 0; j0 < NV; j0 += JG) {
+        v4f sum[JG];
         for (int q = 0; q < S; ++q) {
-            const float *src = slots + (size_t)q * FL + 4 * j * NTHR + tid;
-            v4f v;
+            v4f v[JG];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = __hip_atomic_load(src + e * NTHR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sum = q == 0 ? v : sum + v;
+            for (int jj = 0; jj < JG; ++jj)
+                if (j0 + jj < NV)
+                    v[jj] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, at(q, j0 + jj), 0, DEV));
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj)
+                if (j0 + jj < NV)
+                    sum[jj] = q == 0 ? v[jj] : sum[jj] + v[jj];
         }
-        set(j, sum);
+#pragma unroll
+        for (int jj = 0; jj < JG; ++jj)
+            if (j0 + jj < NV)
+                set(j0 + jj, sum[jj]);
     }
     if (tid == 0)
         __hip_atomic_store(p.flags + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
