@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -391,8 +392,55 @@ struct Config {
 //     (32 x 4096 x 14336: 14.5 us on stream_2x1_k4 -> 12.7);
 //   * 65-128 rows on narrow N that would run the 64 x 128 stream tile: the
 //     64 x 64 four-slot tile in two K parts (below).
+// Environment overrides of the default path, read once per process:
+//   MXG_CONFIG=<variant>[:<K parts>]  the default path runs that
+//     configuration instead of its own choice, for every shape (tuning; a
+//     configuration that does not apply to a call's shape returns
+//     MXG_ERR_CONFIG, one that needs more workspace than the call has
+//     MXG_ERR_WORKSPACE, an unknown variant name MXG_ERR_CONFIG);
+//   MXG_LOG=1  every default-path call prints its format, shape and
+//     configuration to stderr.
+struct EnvOverrides {
+    int variant = -1;   // -1: none
+    int splits = 1;
+    bool bad = false;   // MXG_CONFIG set but not a variant name / part count
+    bool log = false;
+};
+
+const EnvOverrides &env_overrides()
+{
+    static const EnvOverrides env = [] {
+        EnvOverrides o;
+        const char *lg = getenv("MXG_LOG");
+        o.log = lg && *lg && strcmp(lg, "0") != 0;
+        const char *cfg = getenv("MXG_CONFIG");
+        if (!cfg || !*cfg)
+            return o;
+        const char *colon = strchr(cfg, ':');
+        const size_t len = colon ? (size_t)(colon - cfg) : strlen(cfg);
+        for (int v = 0; v < kNumVariants; ++v)
+            if (strlen(kVariants[v].name) == len && strncmp(kVariants[v].name, cfg, len) == 0)
+                o.variant = v;
+        if (colon) {
+            char *end = nullptr;
+            const long parts = strtol(colon + 1, &end, 10);
+            if (end == colon + 1 || *end || parts < 1 || parts > kMaxSplits)
+                o.bad = true;
+            else
+                o.splits = (int)parts;
+        }
+        if (o.variant < 0)
+            o.bad = true;
+        return o;
+    }();
+    return env;
+}
+
 Config pick_config(int is_fp4, int64_t M, int64_t N, int64_t K, bool with_ws)
 {
+    const EnvOverrides &env = env_overrides();
+    if (env.variant >= 0)
+        return Config{env.variant, with_ws ? env.splits : 1};
     Config cf{pick_variant(is_fp4, M, N, K), 1};
     if (!with_ws)
         return cf;
@@ -788,10 +836,25 @@ int run_default(int is_fp4, const void *a, const void *b, const void *sa, const 
     rc = validate_ws(ws, ws_bytes);
     if (rc)
         return rc;
+    const EnvOverrides &env = env_overrides();
+    if (env.bad)
+        return MXG_ERR_CONFIG;
     Config cf = pick_config(is_fp4, M, N, K, true);
-    // a missing or short workspace: the whole-K configuration (correct, maybe slower)
-    if (cf.splits > 1 && (!ws || ws_bytes < splitk_bytes(kVariants[cf.variant], cf.splits, M, N)))
+    if (env.variant >= 0) {
+        // a configuration forced through MXG_CONFIG: as mx_scaled_mm_config
+        rc = check_split(kVariants[cf.variant], is_fp4, M, N, K, cf.splits);
+        if (rc)
+            return rc;
+        if (cf.splits > 1 && (!ws || ws_bytes < splitk_bytes(kVariants[cf.variant], cf.splits, M, N)))
+            return MXG_ERR_WORKSPACE;
+    } else if (cf.splits > 1 && (!ws || ws_bytes < splitk_bytes(kVariants[cf.variant], cf.splits, M, N))) {
+        // a missing or short workspace: the whole-K configuration (correct, maybe slower)
         cf = pick_config(is_fp4, M, N, K, false);
+    }
+    if (env.log)
+        fprintf(stderr, "mxgemm: %s M=%lld N=%lld K=%lld -> %s, %d K part%s%s\n", is_fp4 ? "mxfp4" : "mxfp8",
+                (long long)M, (long long)N, (long long)K, kVariants[cf.variant].name, cf.splits,
+                cf.splits == 1 ? "" : "s", env.variant >= 0 ? " (MXG_CONFIG)" : "");
     rc = check_device();
     if (rc)
         return rc;
@@ -826,7 +889,15 @@ int mx_scaled_mm_noalloc(int is_fp4, const void *a, const void *b, const void *a
     int rc = validate(a, b, a_scale, b_scale, c, M, N, K, out_dtype);
     if (rc)
         return rc;
+    const EnvOverrides &env = env_overrides();
+    if (env.bad)
+        return MXG_ERR_CONFIG;
     const Config cf = pick_config(is_fp4, M, N, K, true);
+    if (env.variant >= 0) {
+        rc = check_split(kVariants[cf.variant], is_fp4, M, N, K, cf.splits);
+        if (rc)
+            return rc;
+    }
     if (splitk_bytes(kVariants[cf.variant], cf.splits, M, N) > kScratchBytes)
         return MXG_ERR_SCRATCH;
     rc = check_device();
@@ -858,7 +929,12 @@ int mx_default_config(int is_fp4, int64_t M, int64_t N, int64_t K, int with_work
     const int rc = check_shape(M, N, K);
     if (rc)
         return rc;
+    const EnvOverrides &env = env_overrides();
+    if (env.bad)
+        return MXG_ERR_CONFIG;
     const Config cf = pick_config(is_fp4 ? 1 : 0, M, N, K, with_workspace != 0);
+    if (env.variant >= 0 && check_split(kVariants[cf.variant], is_fp4 ? 1 : 0, M, N, K, cf.splits))
+        return MXG_ERR_CONFIG;
     if (splits)
         *splits = cf.splits;
     return cf.variant;

@@ -115,6 +115,18 @@ typedef enum {
  *
  * Returns MXG_OK after enqueueing, or an error status with nothing
  * enqueued (MXG_ERR_PTR_ALIGN also for a workspace not 16-byte aligned).
+ *
+ * Environment (read once, at the first call of the process; also honoured
+ * by mx_scaled_mm_noalloc, mx_default_config and
+ * mx_scaled_mm_workspace_bytes):
+ *   MXG_CONFIG=<variant name>[:<K parts>]  run that configuration instead
+ *     of the library's choice, for every shape (tuning; names from
+ *     mx_variant_name).  A configuration that does not apply to a call's
+ *     shape returns MXG_ERR_CONFIG, one whose K parts need more workspace
+ *     than the call brings MXG_ERR_WORKSPACE, and a value that names no
+ *     variant or part count MXG_ERR_CONFIG for every call.
+ *   MXG_LOG=1  each call prints its format, M, N, K and the configuration
+ *     it runs (variant, K parts) to stderr.
  */
 int mx_scaled_mm_fp4(const void *a, const void *b, const void *a_scale, const void *b_scale,
                      void *c, int64_t M, int64_t N, int64_t K, int out_dtype, void *workspace,

@@ -418,3 +418,64 @@ def test_noalloc_argument_checks(lib):
     # its scratch holds the largest default split-K workspace
     assert lib.mx_noalloc_scratch_bytes() >= lib.mx_scaled_mm_workspace_bytes(1, 512, 4096, 14336) > 0
     assert b"scratch" in lib.mx_status_string(-10)
+
+
+# The environment overrides of the default path (MXG_CONFIG / MXG_LOG) are
+# read once per process, so each setting runs in a child process.  Only
+# calls that fail before the device check are made (no GPU is needed, and
+# no kernel could start on the fake pointers).
+_ENV_PROBE = r"""
+import ctypes, json, sys
+L = ctypes.CDLL(sys.argv[1])
+I64, INT, P, SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+L.mx_default_config.argtypes = [INT, I64, I64, I64, INT, ctypes.POINTER(INT)]
+L.mx_scaled_mm_workspace_bytes.argtypes = [INT, I64, I64, I64]
+L.mx_scaled_mm_workspace_bytes.restype = SZ
+L.mx_config_workspace_bytes.argtypes = [INT, INT, I64, I64]
+L.mx_config_workspace_bytes.restype = SZ
+L.mx_variant_name.restype = ctypes.c_char_p
+L.mx_scaled_mm_fp4.argtypes = [P] * 5 + [I64] * 3 + [INT, P, SZ, P]
+sp = INT(0)
+out = {}
+v = L.mx_default_config(1, 128, 4096, 14336, 1, ctypes.byref(sp))
+out["ws"] = [v, sp.value, L.mx_variant_name(v).decode() if v >= 0 else None]
+v2 = L.mx_default_config(1, 128, 4096, 14336, 0, ctypes.byref(sp))
+out["nows"] = [v2, sp.value]
+out["ws_bytes"] = [L.mx_scaled_mm_workspace_bytes(1, 128, 4096, 14336),
+                   L.mx_config_workspace_bytes(v, 2, 128, 4096) if v >= 0 else -1]
+out["long_k"] = L.mx_default_config(1, 32, 14336, 65536, 1, ctypes.byref(sp))
+A = 1 << 20
+if sys.argv[2] == "call":
+    out["call"] = L.mx_scaled_mm_fp4(A, A, A, A, A, 128, 4096, 14336, 0, None, 0, None)
+print(json.dumps(out))
+"""
+
+
+def _env_probe(value, call):
+    import json
+    import subprocess
+    import sys
+    env = {k: v for k, v in os.environ.items() if not k.startswith("MXG_")}
+    env["MXG_CONFIG"] = value
+    r = subprocess.run([sys.executable, "-c", _ENV_PROBE, LIB, "call" if call else "nocall"],
+                       env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_env_config_override(lib):
+    # a valid override: reported by mx_default_config, sized by
+    # mx_scaled_mm_workspace_bytes, and a call short of workspace refused
+    out = _env_probe("tile_64x64_r4:2", call=True)
+    assert out["ws"][2] == "tile_64x64_r4" and out["ws"][1] == 2
+    assert out["nows"] == [out["ws"][0], 1]
+    assert out["ws_bytes"][0] == out["ws_bytes"][1] > 0
+    assert out["long_k"] == out["ws"][0]           # the 64x64 tile takes any K
+    assert out["call"] == -6                       # MXG_ERR_WORKSPACE
+    # a variant whose K limit the shape exceeds: MXG_ERR_CONFIG for that shape
+    out = _env_probe("decode_32x64", call=False)
+    assert out["ws"][0] == -9 and out["long_k"] == -9
+    # names no variant / no part count: every call MXG_ERR_CONFIG
+    for bad in ("no_such_variant", "tile_128x128:x", "tile_128x128:0", "tile_128x128:65"):
+        out = _env_probe(bad, call=True)
+        assert out["ws"][0] == -9 and out["nows"][0] == -9 and out["call"] == -9, bad
