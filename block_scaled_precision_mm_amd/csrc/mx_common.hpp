@@ -46,6 +46,8 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 
 enum { FMT_FP8 = 0, FMT_FP4 = 1 };
+// Unscaled 16-bit operands (the dense product on the tile kernel)
+enum { FMT_BF16 = 2, FMT_F16 = 3 };
 // Output kinds.  OUT_MX8 / OUT_MX4 (fused epilogue only): the BF16-rounded
 // result MX-quantized along N (E4M3 / E2M1 codes + one E8M0 per 32 columns).
 enum { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2, OUT_MX8 = 3, OUT_MX4 = 4 };
@@ -55,11 +57,23 @@ template <> struct FmtTraits<FMT_FP8> {
     static constexpr int step_bytes = 128;  // bytes of one 128-deep K step per row
     static constexpr int nvec = 2;          // 16-byte pieces per lane per step
     static constexpr int mfma_code = 0;     // instruction format code for E4M3
+    static constexpr bool scaled = true;    // E8M0 codes per 32 K values
 };
 template <> struct FmtTraits<FMT_FP4> {
     static constexpr int step_bytes = 64;
     static constexpr int nvec = 1;
     static constexpr int mfma_code = 4;     // instruction format code for E2M1
+    static constexpr bool scaled = true;
+};
+template <> struct FmtTraits<FMT_BF16> {
+    static constexpr int step_bytes = 256;
+    static constexpr int nvec = 1;
+    static constexpr bool scaled = false;
+};
+template <> struct FmtTraits<FMT_F16> {
+    static constexpr int step_bytes = 256;
+    static constexpr int nvec = 1;
+    static constexpr bool scaled = false;
 };
 
 // Kernel arguments shared by every kernel family.

@@ -96,16 +96,19 @@ struct TileGeom {
     static constexpr int BM = 64 * MT, BN = 64 * NT;    // workgroup tile
     static constexpr int ROWS = BM + BN;                 // A rows then B rows
     static constexpr int SW = 128;                       // row bytes per super-stage
-    static constexpr int KSS = SW * (F == FMT_FP4 ? 2 : 1);   // K values per super-stage
-    static constexpr int SUB = KSS / 64;                 // 32x32x64 sub-steps per super-stage
+    static constexpr bool SCALED = FmtTraits<F>::scaled; // E8M0 codes (else 16-bit operands)
+    // K values per super-stage: 256 (E2M1), 128 (E4M3), 64 (BF16 / FP16)
+    static constexpr int KSS = SCALED ? SW * (F == FMT_FP4 ? 2 : 1) : SW / 2;
+    // MFMA sub-steps per super-stage: 32x32x64 (MX) or 32x32x16 (16-bit)
+    static constexpr int SUB = SCALED ? KSS / 64 : KSS / 16;
     static constexpr int SLOT = ROWS * SW;               // one code slot (unpadded, swizzled)
     static constexpr int RPL = 1024 / SW;                // rows per 1 KB load
     static constexpr int LPR = SW / 16;                  // lanes per row of a load
     static constexpr int LB = ROWS / RPL / 4;            // 1 KB loads per wave per super-stage
     // scale codes: 16 bytes per row per period of 4 steps (512 K)
-    static constexpr int P = 512 / KSS;                  // super-stages per period
+    static constexpr int P = SCALED ? 512 / KSS : 2;     // super-stages per period
     static constexpr int SJOBS = cdiv_c(ROWS, 64);       // 64-row scale loads per period
-    static constexpr int LS = cdiv_c(SJOBS, 4);          // per wave (jobs past SJOBS load nothing)
+    static constexpr int LS = SCALED ? cdiv_c(SJOBS, 4) : 0;   // per wave (jobs past SJOBS load nothing)
     static constexpr int SROWS = 64 * 4 * LS;            // scale rows incl. padding
     static constexpr int SCB = SROWS * 16;               // one scale buffer: [dword][row]
     static constexpr int BYTES = NS * SLOT + 2 * SCB;
@@ -169,6 +172,21 @@ __device__ __forceinline__ void static_for(Fn &&f)
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// 16-bit operands: v_mfma_f32_32x32x16_{bf16,f16}, lane (r, g) holding 8 K
+// values of row r (B rows as the first operand, A rows as the second)
+typedef __bf16 tile_bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 tile_f16x8 __attribute__((ext_vector_type(8)));
+template <int F>
+__device__ __forceinline__ v16f mfma16(const u4v &x, const u4v &y, v16f acc)
+{
+    if constexpr (F == FMT_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(tile_bf16x8, x),
+                                                       __builtin_bit_cast(tile_bf16x8, y), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(tile_f16x8, x),
+                                                      __builtin_bit_cast(tile_f16x8, y), acc, 0, 0, 0);
+}
+
 // SEL: the byte of each scale register that holds the lane's code
 template <int F, int SEL = 0>
 __device__ __forceinline__ v16f mfma32(v8i x, unsigned sx, v8i y, unsigned sy, v16f acc)
@@ -210,7 +228,7 @@ void mx_gemm_tile(GemmArgs p)
     __shared__ __attribute__((aligned(1024))) char slot1[G::SLOT];
     __shared__ __attribute__((aligned(1024))) char slot2[NS == 4 ? G::SLOT : 16];
     __shared__ __attribute__((aligned(1024))) char slot3[NS == 4 ? G::SLOT : 16];
-    __shared__ __attribute__((aligned(1024))) char sbuf[2 * G::SCB];
+    __shared__ __attribute__((aligned(1024))) char sbuf[G::SCALED ? 2 * G::SCB : 16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -233,7 +251,7 @@ void mx_gemm_tile(GemmArgs p)
     } else {
         tile_of(blockIdx.x, (p.M + G::BM - 1) / G::BM, nbn, tm, tn);
         // split-K: this workgroup's K part (whole periods of four steps)
-        if constexpr (!EPI)
+        if constexpr (!EPI && G::SCALED)
             select_split<F>(p, 4);
     }
     const int m0 = tm * G::BM, n0 = tn * G::BN;
@@ -353,7 +371,9 @@ void mx_gemm_tile(GemmArgs p)
     constexpr int NV = FmtTraits<F>::nvec;
     using Frag = TileFrag<F, MT, NT>;
     // whether sub-step kk reads scale dwords (else it reuses the previous one's)
-    constexpr auto new_scales = [](int kk) { return F == FMT_FP4 ? kk % G::SUB == 0 : kk % 2 == 0; };
+    constexpr auto new_scales = [](int kk) {
+        return !G::SCALED ? false : F == FMT_FP4 ? kk % G::SUB == 0 : kk % 2 == 0;
+    };
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
     auto read = [&](Frag &R, auto k, int u, auto kkc, const Frag *prev) {
         constexpr int kk = decltype(kkc)::value;
@@ -363,7 +383,10 @@ void mx_gemm_tile(GemmArgs p)
         const char *sc = sbuf + ((u / G::P) & 1) * G::SCB + step * G::SROWS * 4;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int c = F == FMT_FP4 ? h + 4 * g : 4 * h + 2 * v + g;
+            // (16-bit operands: sub-step h takes 8 K values of each half
+            // super-stage, like E2M1; with no scale codes any fixed K order
+            // shared by A and B computes the product)
+            const int c = F == FMT_FP8 ? 4 * h + 2 * v + g : h + 4 * g;
 #pragma unroll
             for (int i = 0; i < MT; ++i)
                 R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
@@ -371,6 +394,8 @@ void mx_gemm_tile(GemmArgs p)
             for (int j = 0; j < NT; ++j)
                 R.b[j][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(brow + 32 * j, c));
         }
+        if constexpr (!G::SCALED)
+            return;
         // sub-steps that share a scale dword take it from the first one's
         // registers
         if constexpr (!new_scales(kk)) {
@@ -409,17 +434,21 @@ void mx_gemm_tile(GemmArgs p)
 #pragma unroll
         for (int ij = decltype(lo)::value; ij < decltype(hi)::value; ++ij) {
                 const int i = ij / NT, j = ij % NT;
-                v8i x, y;
-                if constexpr (F == FMT_FP4) {
-                    const u4v bx = R.b[j][0], ay = R.a[i][0];
-                    x = v8i{(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w, 0, 0, 0, 0};
-                    y = v8i{(int)ay.x, (int)ay.y, (int)ay.z, (int)ay.w, 0, 0, 0, 0};
+                if constexpr (!G::SCALED) {
+                    acc[i][j] = mfma16<F>(R.b[j][0], R.a[i][0], acc[i][j]);
                 } else {
-                    const u4v b0 = R.b[j][0], b1 = R.b[j][NV - 1], a0 = R.a[i][0], a1 = R.a[i][NV - 1];
-                    x = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                    y = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    v8i x, y;
+                    if constexpr (F == FMT_FP4) {
+                        const u4v bx = R.b[j][0], ay = R.a[i][0];
+                        x = v8i{(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w, 0, 0, 0, 0};
+                        y = v8i{(int)ay.x, (int)ay.y, (int)ay.z, (int)ay.w, 0, 0, 0, 0};
+                    } else {
+                        const u4v b0 = R.b[j][0], b1 = R.b[j][NV - 1], a0 = R.a[i][0], a1 = R.a[i][NV - 1];
+                        x = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                        y = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    }
+                    acc[i][j] = mfma32<F, F == FMT_FP4 ? kk % G::SUB : 0>(x, xs[j], y, ys[i], acc[i][j]);
                 }
-                acc[i][j] = mfma32<F, F == FMT_FP4 ? kk % G::SUB : 0>(x, xs[j], y, ys[i], acc[i][j]);
         }
     };
 

@@ -716,6 +716,27 @@ typedef void (*DenseFn)(DenseArgs);
 #define MXG_DLAYOUTS(T) {{MXG_DFN4(T, 0, 0), MXG_DFN4(T, 0, 1)}, {MXG_DFN4(T, 1, 0), MXG_DFN4(T, 1, 1)}}
 const DenseFn kDense[2][2][2][3] = {MXG_DLAYOUTS(DENSE_BF16), MXG_DLAYOUTS(DENSE_F16)};
 
+// NT (both operands K-contiguous, the MFMA's own layout): the tile kernel
+// with 16-bit operands (its loads, LDS slots and pipeline; no scale codes).
+// [dtype][tile: 256x256, 128x256, 128x128][out]
+#define MXG_D16(F, MT, NT)                                                                       \
+    {&mx_gemm_tile<F, MT, NT, OUT_BF16>, &mx_gemm_tile<F, MT, NT, OUT_F16>,                       \
+     &mx_gemm_tile<F, MT, NT, OUT_F32>}
+const KernelFn kDenseNT[2][3][3] = {
+    {MXG_D16(FMT_BF16, 4, 4), MXG_D16(FMT_BF16, 2, 4), MXG_D16(FMT_BF16, 2, 2)},
+    {MXG_D16(FMT_F16, 4, 4), MXG_D16(FMT_F16, 2, 4), MXG_D16(FMT_F16, 2, 2)}};
+
+// The largest of the three tiles that still gives at least 192 workgroups
+// (the same rule as the MX products'), else 128 x 128.
+int dense_nt_tile(int64_t M, int64_t N)
+{
+    if (M > 128 && cdiv(M, 256) * cdiv(N, 256) >= 192)
+        return 0;
+    if (M >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 192)
+        return 1;
+    return 2;
+}
+
 int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b, void *c,
               int64_t M, int64_t N, int64_t K, int out_dtype, hipStream_t stream)
 {
@@ -738,6 +759,33 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
         return MXG_ERR_SHAPE;
     if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
         return MXG_ERR_PTR_ALIGN;
+    if (!trans_a && trans_b) {
+        const int t = dense_nt_tile(M, N);
+        const int bm = t == 0 ? 256 : 128, bn = t == 2 ? 128 : 256;
+        const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
+        if (tiles > INT32_MAX)
+            return MXG_ERR_SHAPE;
+        int rc = check_device();
+        if (rc)
+            return rc;
+        GemmArgs p;
+        memset(&p, 0, sizeof(p));
+        p.a = (const uint8_t *)a;
+        p.b = (const uint8_t *)b;
+        p.c = c;
+        p.M = (int)M;
+        p.N = (int)N;
+        p.row_bytes = (unsigned)(2 * K);
+        p.kbytes = p.row_bytes;
+        p.splits = 1;
+        hipLaunchKernelGGL(kDenseNT[dtype][t][out_dtype], dim3((unsigned)tiles), dim3(256), 0, stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return MXG_ERR_HIP;
+        }
+        return MXG_OK;
+    }
     const int64_t gx = cdiv(N, DenseTile::BN), gy = cdiv(M, DenseTile::BM);
     if (gx > INT32_MAX || gy > 65535)
         return MXG_ERR_SHAPE;
