@@ -68,6 +68,11 @@
 // super-stages past K (and rows past M or N) load zero codes through
 // out-of-range offsets and have zero scale codes, and add exactly +0.
 //
+// 16-bit operands (F = FMT_BF16 / FMT_F16: the dense NT product).  A
+// v_mfma_f32_32x32x16 sub-step reads 32 bytes per row, lane half g 16 of
+// them, as an E2M1 sub-step does, so the same super-stages, slots and
+// pipeline run it; there are no scale codes to load, write or read.
+//
 // Waves.  Four waves in 2 x 2, each owning a (32*MT) x (32*NT) part of the
 // (64*MT) x (64*NT) workgroup tile; at MT = NT = 4 the 256 accumulator
 // registers per lane fill the accumulation register file.
