@@ -133,7 +133,7 @@ struct TileGeom {
     static_assert(NS == 2 || NS == 4, "two or four code slots");
     static_assert(P % 2 == 0, "a period covers whole pairs of code slots");
     static_assert((ROWS / RPL) % 4 == 0, "load blocks must spread evenly over 4 waves");
-    static_assert(BM % RPL == 0, "A and B rows never share a load block");
+    static_assert(BM % (4 * RPL) == 0, "A and B rows never share a load block, and the first BM / (4 RPL) of a wave's are A's");
     static_assert(NS * LB + SLEAD * LS < 64, "outstanding loads must fit the vmcnt field");
     // byte offset of 16-byte chunk c of tile row `row` in a code slot: the
     // chunk's place XORed with the row so that the 16 rows of a fragment
@@ -180,6 +180,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // 16-bit operands: v_mfma_f32_32x32x16_{bf16,f16}, lane (r, g) holding 8 K
 // values of row r (B rows as the first operand, A rows as the second)
 typedef __bf16 tile_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short tile_s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 tile_f16x8 __attribute__((ext_vector_type(8)));
 template <int F>
 __device__ __forceinline__ v16f mfma16(const u4v &x, const u4v &y, v16f acc)
@@ -217,13 +218,19 @@ struct TileFrag {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2>
+// TB (16-bit operands only): B is stored [K][N] (N-contiguous, the dense NN
+// layout); its part of a slot holds the super-stage's 64 K rows of the
+// tile's BN columns, and its fragments are read with gfx950's transposing
+// LDS read (see "B stored [K][N]" below).
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2, int TB = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
     static_assert(EPI || OUT <= OUT_F32, "MX output kinds need the fused epilogue");
     using G = TileGeom<F, MT, NT, NS>;
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
+    static_assert(!TB || (!G::SCALED && !GRP && !EPI && NT >= 2 && (NT & (NT - 1)) == 0),
+                  "B stored [K][N]: 16-bit, plain, BN >= 128 and a power of two");
     // The two code slots and the scale buffers are separate LDS objects: the
     // compiler then knows that a fragment read of one slot cannot touch what
     // a direct-to-LDS load still in flight writes into the other, and does
@@ -264,8 +271,11 @@ void mx_gemm_tile(GemmArgs p)
     const int nrows = min(G::BN, p.N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(p.a + (size_t)m0 * p.row_bytes, part_range(mrows, p.row_bytes, p.kbytes));
+    // (B stored [K][N]: the whole operand, K rows of N columns; rows past K
+    // read zeros)
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.b + (size_t)n0 * p.row_bytes, part_range(nrows, p.row_bytes, p.kbytes));
+        TB ? make_rsrc(p.b, p.kbytes * (unsigned)p.N)
+           : make_rsrc(p.b + (size_t)n0 * p.row_bytes, part_range(nrows, p.row_bytes, p.kbytes));
     const __amdgpu_buffer_rsrc_t rsa =
         make_rsrc(p.sa + (size_t)m0 * p.srow_bytes, part_range(mrows, p.srow_bytes, 4u * p.nsteps));
     const __amdgpu_buffer_rsrc_t rsb =
@@ -286,14 +296,28 @@ void mx_gemm_tile(GemmArgs p)
     const unsigned kb = p.kbytes, ktail = kb % G::SW;
     unsigned voff[G::LB], vtail[G::LB];
     bool vla[G::LB];
+    // B stored [K][N]: a 1 KB block holds KPB whole K rows of the tile's BN
+    // columns (BCH 16-byte chunks each); chunk c of K row k sits at place
+    // c ^ 4 (k mod 4), so that the eight K rows and four chunks of one
+    // transposing read fall on different bank groups
+    constexpr int BCH = G::BN / 8, KPB = 1024 / (2 * G::BN);
 #pragma unroll
     for (int j = 0; j < G::LB; ++j) {
         const int q = wave + 4 * j;
         const int row = G::RPL * q + lrow;                    // tile row in [A | B]
         const unsigned cb = 16u * (unsigned)((lane % G::LPR) ^ G::swz(row));   // this lane's chunk, in bytes
-        vla[j] = G::RPL * q < G::BM;                          // A and B rows never share a block
+        // A and B rows never share a block: block q = wave + 4j is an A block
+        // when RPL * q < BM, i.e. (BM / RPL being a multiple of 4, wave < 4)
+        // when j < BM / (4 RPL) -- known at compile time
+        vla[j] = j < G::BM / (4 * G::RPL);
         voff[j] = (unsigned)(vla[j] ? row : row - G::BM) * p.row_bytes + cb;
         vtail[j] = cb < ktail ? voff[j] : kOutOfRange;
+        if (TB && !vla[j]) {
+            const int kr = KPB * (q - G::BM / G::RPL) + lane / BCH;   // K row of the super-stage
+            const int n = n0 + 8 * ((lane % BCH) ^ (4 * (kr & 3)));
+            voff[j] = n < p.N ? ((unsigned)kr * (unsigned)p.N + (unsigned)n) * 2u : kOutOfRange;
+            vtail[j] = voff[j];   // (a partial super-stage's rows past K are past the range)
+        }
     }
     // slot of super-stage u: u mod NS, always known at compile time
     auto slot_of = [&](auto k) -> char * {
@@ -314,18 +338,23 @@ void mx_gemm_tile(GemmArgs p)
         // per super-stage for the compiler to precompute and hold)
         const unsigned ko = (unsigned)u * G::SW;
         const bool whole = ko + G::SW <= kb, live = ko < kb;
+        // B stored [K][N]: the super-stage's 64 K rows start N * 128 bytes
+        // per super-stage in; rows past K are past the buffer range
+        const unsigned kob = live ? (unsigned)u * 128u * (unsigned)p.N : 0u;
 #pragma unroll
         for (int j = 0; j < G::LB; ++j) {
             const int q = wave + 4 * j;
-            // past this K range: an offset no buffer range reaches (zeros)
-            const unsigned off = whole ? voff[j] : live ? vtail[j] : kOutOfRange;
+            // past this K range: an offset no buffer range reaches (zeros);
+            // B stored [K][N] adds its super-stage's rows (0 when not live)
+            const unsigned off = (whole ? voff[j] : live ? vtail[j] : kOutOfRange) + (TB && !vla[j] ? kob : 0u);
             // (a branch, not a select of the two resources: the latter is
             // rejected by the host pass of a __global__ template, which
             // then silently emits no launch stub)
+            const unsigned so = TB && !vla[j] ? 0u : ko;   // (B stored [K][N]: all in off)
             if (vla[j])
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * q), 16, off, ko, 0, CPOL_NONE);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * q), 16, off, so, 0, CPOL_NONE);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + 1024 * q), 16, off, ko, 0, CPOL_NONE);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + 1024 * q), 16, off, so, 0, CPOL_NONE);
         }
     };
 
@@ -395,9 +424,39 @@ void mx_gemm_tile(GemmArgs p)
 #pragma unroll
             for (int i = 0; i < MT; ++i)
                 R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
+            if constexpr (TB) {
+                // B stored [K][N], read transposed: for each group of 16
+                // lanes the instruction takes four K rows of 16 columns,
+                // lanes 4i .. 4i+3 giving row i's four 8-byte pieces, and
+                // hands lane t of the group column t of the four rows.  Lane
+                // (r, g) thus gets column r of the fragment at K rows
+                // 8c .. 8c+3 from one read and 8c+4 .. 8c+7 from another
+                // (c = h + 4g, the K values its A fragment holds).
+                const char *bs = slot + G::BM * G::SW;
+                const int jr = (r & 15) >> 2;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                R.b[j][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(brow + 32 * j, c));
+                for (int j = 0; j < NT; ++j) {
+                    const int cn = 4 * (wn * NT + j) + 2 * (r >> 4) + ((r & 3) >> 1);   // column chunk
+                    u2v half[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int k = 8 * c + 4 * e + jr;
+                        // (the mask, a no-op here, bounds the offset to the B
+                        // region: the compiler then sees which slot the read
+                        // touches and does not wait for loads into the other)
+                        const int o = (k * (2 * G::BN) + 16 * (cn ^ (4 * (k & 3))) + 8 * (r & 1)) & (G::BN * G::SW - 1);
+                        const char *a = bs + o;
+                        half[e] = __builtin_bit_cast(
+                            u2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                     (__attribute__((address_space(3))) tile_s16x4 *)(a)));
+                    }
+                    R.b[j][v] = u4v{half[0].x, half[0].y, half[1].x, half[1].y};
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    R.b[j][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(brow + 32 * j, c));
+            }
         }
         if constexpr (!G::SCALED)
             return;
@@ -458,7 +517,7 @@ void mx_gemm_tile(GemmArgs p)
     };
 
     constexpr int NM = MT * NT;                  // MFMAs per sub-step
-    constexpr int NCR = NV * (MT + NT);          // fragment reads per sub-step
+    constexpr int NCR = NV * (MT + (TB ? 2 : 1) * NT);   // fragment reads per sub-step
     Frag R[2];
 
     // prologue: period 0's scale codes written, the next staged;

@@ -112,26 +112,29 @@ def test_large_sampled(mx):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("tb", [1, 0], ids=["NT", "NN"])
 @pytest.mark.parametrize("shape", [(4096, 3072, 264), (2048, 3072, 520), (1000, 1000, 72)],
                          ids=["256x256tile", "128x256tile", "128x128tile"])
-def test_nt_tiles_sampled(mx, dtype, shape):
-    # the NT layout runs on the 256 x 256, 128 x 256 or 128 x 128 tile by the
+def test_tile_layouts_sampled(mx, dtype, tb, shape):
+    # NT and NN run on the tile kernel (NN with B's slots K-row-major, read
+    # transposed), on the 256 x 256, 128 x 256 or 128 x 128 tile by the
     # number of output tiles; K not a multiple of the 64-deep super-stage;
     # sampled outputs plus the last row and column against the oracle
     M, N, K = shape
-    rng = np.random.default_rng(M + N + K)
+    rng = np.random.default_rng(M + N + K + tb)
     A = bits(rng.standard_normal((M, K)), dtype)
-    B = bits(rng.standard_normal((N, K)), dtype)
-    print("dense NT tiles", dtype, shape, flush=True)
-    c32 = run(mx, dtype, 0, 1, A, B, M, N, K, "f32")
+    B = bits(rng.standard_normal((K, N)), dtype)            # the logical [K][N] operand
+    b_st = stored(B, tb)
+    print("dense tile", dtype, "NT" if tb else "NN", shape, flush=True)
+    c32 = run(mx, dtype, 0, tb, A, b_st, M, N, K, "f32")
     ms = np.concatenate([rng.integers(0, M, 3000), np.full(64, M - 1), rng.integers(0, M, 64)])
     ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 64), np.full(64, N - 1)])
     Av = oracle.dense_values(dtype, A, (M, K))
-    Bv = oracle.dense_values(dtype, B, (N, K))
-    ref = np.einsum("ik,ik->i", Av[ms], Bv[ns])
-    S = np.einsum("ik,ik->i", np.abs(Av[ms]), np.abs(Bv[ns]))
+    Bv = oracle.dense_values(dtype, B, (K, N))
+    ref = np.einsum("ik,ki->i", Av[ms], Bv[:, ns])
+    S = np.einsum("ik,ki->i", np.abs(Av[ms]), np.abs(Bv[:, ns]))
     tol = (K / 16 + 16) * 2.0 ** -24 * S + 2.0 ** -126 * K
     assert np.all(np.abs(c32[ms, ns] - ref) <= tol)
     for out, rnd in (("bf16", oracle.round_bf16), ("f16", oracle.round_f16)):
-        b16 = run(mx, dtype, 0, 1, A, B, M, N, K, out)
+        b16 = run(mx, dtype, 0, tb, A, b_st, M, N, K, out)
         assert np.array_equal(b16, rnd(c32)), "%s %s != RNE(f32)" % (shape, out)
