@@ -486,9 +486,9 @@ def bench_dense(args):
         ach = flops / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / DENSE_PEAK_TFLOPS, 4), "traffic": None}
-    # NT runs on the tile kernel with 16-bit operands (its tile chosen by the
-    # number of output tiles), the other layouts on the transposing kernel
-    kname = "dense_tile_nt" if lay == "nt" else "dense_128x128_" + lay
+    # the tile kernel with 16-bit operands (its tile chosen by the number of
+    # output tiles; operands contiguous along M or N read transposed)
+    kname = "dense_tile_" + lay
     roof.update({"kernel": kname, "algorithmic_bytes": int(alg),
                  "kernel_us": round(ms * 1e3, 3), "roofline_us": round(max(t_hbm, t_mfma) * 1e6, 3)})
     out = {

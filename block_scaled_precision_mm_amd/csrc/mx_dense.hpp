@@ -8,9 +8,11 @@
 // (TB = 0) or [N][K] (TB = 1).  "NT" -- both operands K-contiguous -- is the
 // MFMA's own layout; in the others one or both operands are contiguous
 // along M or N and are transposed on their way into LDS.  The library
-// runs NT on the tile kernel instead (mx_tile.hpp, 16-bit operands: its
-// direct-to-LDS loads and deeper pipeline took 8192^3 from 1452 to 884 us);
-// this kernel serves the other three layouts (and still takes NT).
+// runs every layout on the tile kernel instead (mx_tile.hpp, 16-bit
+// operands, an operand contiguous along M or N kept in K rows and read with
+// transposing LDS reads: 8192^3 in 913-925 us against 1452-2241 here); this
+// kernel is the fallback where an operand stored [K][M] / [K][N] is too
+// large for the tile kernel's 32-bit offsets.
 //
 // Instruction.  v_mfma_f32_32x32x16_{bf16,f16}: lane l = 32g + r supplies
 // row r of its 32-row operand block with the 8 K values [8g, 8g+8) of the

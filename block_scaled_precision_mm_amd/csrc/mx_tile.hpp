@@ -218,11 +218,12 @@ struct TileFrag {
 // One workgroup per CU: the accumulators of the largest tiles need the
 // whole register file of a SIMD (the LDS footprint alone would let the
 // compiler aim for two).
-// TB (16-bit operands only): B is stored [K][N] (N-contiguous, the dense NN
-// layout); its part of a slot holds the super-stage's 64 K rows of the
-// tile's BN columns, and its fragments are read with gfx950's transposing
-// LDS read (see "B stored [K][N]" below).
-template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2, int TB = 0>
+// TA / TB (16-bit operands only): A is stored [K][M] / B is stored [K][N]
+// (contiguous along M / N, the dense TN, TT and NN layouts); its part of a
+// slot holds the super-stage's 64 K rows of the tile's BM / BN columns, and
+// its fragments are read with gfx950's transposing LDS read (see
+// read_kmajor below).
+template <int F, int MT, int NT, int OUT, int GRP = 0, int EPI = 0, int NS = 2, int TB = 0, int TA = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, MT * NT > 4 ? 1 : 2)))
 void mx_gemm_tile(GemmArgs p)
 {
@@ -231,6 +232,8 @@ void mx_gemm_tile(GemmArgs p)
     static_assert(G::BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
     static_assert(!TB || (!G::SCALED && !GRP && !EPI && NT >= 2 && (NT & (NT - 1)) == 0),
                   "B stored [K][N]: 16-bit, plain, BN >= 128 and a power of two");
+    static_assert(!TA || (!G::SCALED && !GRP && !EPI && MT >= 2 && (MT & (MT - 1)) == 0),
+                  "A stored [K][M]: 16-bit, plain, BM >= 128 and a power of two");
     // The two code slots and the scale buffers are separate LDS objects: the
     // compiler then knows that a fragment read of one slot cannot touch what
     // a direct-to-LDS load still in flight writes into the other, and does
@@ -269,8 +272,10 @@ void mx_gemm_tile(GemmArgs p)
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int mrows = min(G::BM, p.M - m0);
     const int nrows = min(G::BN, p.N - n0);
+    // (A stored [K][M]: the whole operand, as B stored [K][N] below)
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.a + (size_t)m0 * p.row_bytes, part_range(mrows, p.row_bytes, p.kbytes));
+        TA ? make_rsrc(p.a, p.kbytes * (unsigned)p.M)
+           : make_rsrc(p.a + (size_t)m0 * p.row_bytes, part_range(mrows, p.row_bytes, p.kbytes));
     // (B stored [K][N]: the whole operand, K rows of N columns; rows past K
     // read zeros)
     const __amdgpu_buffer_rsrc_t rb =
@@ -301,6 +306,7 @@ void mx_gemm_tile(GemmArgs p)
     // c ^ 4 (k mod 4), so that the eight K rows and four chunks of one
     // transposing read fall on different bank groups
     constexpr int BCH = G::BN / 8, KPB = 1024 / (2 * G::BN);
+    constexpr int ACH = G::BM / 8, KPA = 1024 / (2 * G::BM);   // (A stored [K][M]: the same)
 #pragma unroll
     for (int j = 0; j < G::LB; ++j) {
         const int q = wave + 4 * j;
@@ -317,6 +323,12 @@ void mx_gemm_tile(GemmArgs p)
             const int n = n0 + 8 * ((lane % BCH) ^ (4 * (kr & 3)));
             voff[j] = n < p.N ? ((unsigned)kr * (unsigned)p.N + (unsigned)n) * 2u : kOutOfRange;
             vtail[j] = voff[j];   // (a partial super-stage's rows past K are past the range)
+        }
+        if (TA && vla[j]) {
+            const int kr = KPA * q + lane / ACH;
+            const int m = m0 + 8 * ((lane % ACH) ^ (4 * (kr & 3)));
+            voff[j] = m < p.M ? ((unsigned)kr * (unsigned)p.M + (unsigned)m) * 2u : kOutOfRange;
+            vtail[j] = voff[j];
         }
     }
     // slot of super-stage u: u mod NS, always known at compile time
@@ -338,19 +350,21 @@ void mx_gemm_tile(GemmArgs p)
         // per super-stage for the compiler to precompute and hold)
         const unsigned ko = (unsigned)u * G::SW;
         const bool whole = ko + G::SW <= kb, live = ko < kb;
-        // B stored [K][N]: the super-stage's 64 K rows start N * 128 bytes
-        // per super-stage in; rows past K are past the buffer range
+        // stored [K][M] / [K][N]: the super-stage's 64 K rows start M / N
+        // times 128 bytes per super-stage in; rows past K are past the range
         const unsigned kob = live ? (unsigned)u * 128u * (unsigned)p.N : 0u;
+        const unsigned koa = live ? (unsigned)u * 128u * (unsigned)p.M : 0u;
 #pragma unroll
         for (int j = 0; j < G::LB; ++j) {
             const int q = wave + 4 * j;
             // past this K range: an offset no buffer range reaches (zeros);
-            // B stored [K][N] adds its super-stage's rows (0 when not live)
-            const unsigned off = (whole ? voff[j] : live ? vtail[j] : kOutOfRange) + (TB && !vla[j] ? kob : 0u);
+            // stored [K][..], the super-stage's rows are added (0 when not live)
+            const bool kmaj = vla[j] ? TA : TB;
+            const unsigned off = (whole ? voff[j] : live ? vtail[j] : kOutOfRange) + (!kmaj ? 0u : vla[j] ? koa : kob);
             // (a branch, not a select of the two resources: the latter is
             // rejected by the host pass of a __global__ template, which
             // then silently emits no launch stub)
-            const unsigned so = TB && !vla[j] ? 0u : ko;   // (B stored [K][N]: all in off)
+            const unsigned so = kmaj ? 0u : ko;   // (stored [K][..]: all in off)
             if (vla[j])
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * q), 16, off, so, 0, CPOL_NONE);
             else
@@ -409,6 +423,30 @@ void mx_gemm_tile(GemmArgs p)
         return !G::SCALED ? false : F == FMT_FP4 ? kk % G::SUB == 0 : kk % 2 == 0;
     };
     const int arow = wm * 32 * MT + r, brow = G::BM + wn * 32 * NT + r;
+    // Fragment of an operand stored [K][rows] (its region of a slot: 64 K
+    // rows of `cols` columns, chunk x of K row k at place x ^ 4 (k mod 4)),
+    // read transposed: for each group of 16 lanes the instruction takes four
+    // K rows of 16 columns, lanes 4i .. 4i+3 giving row i's four 8-byte
+    // pieces, and hands lane t of the group column t of the four rows.  So
+    // lane (r, g) gets column 16 (r >> 4) + (r & 15) of the 32 that start at
+    // column chunk cn - 2 (r >> 4) - ((r & 3) >> 1), at K rows 8 c8 .. +3
+    // from one read and 8 c8 + 4 .. +7 from another (c8 = h + 4g: the K
+    // values the other operand's fragment holds).
+    auto read_kmajor = [&](const char *region, const int cols, const int cn, const int c8) -> u4v {
+        const int jr = (r & 15) >> 2;
+        u2v half[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int k = 8 * c8 + 4 * e + jr;
+            // (the mask, a no-op here, bounds the offset to the region: the
+            // compiler then sees which slot the read touches and does not
+            // wait for the loads into the other)
+            const int o = (k * (2 * cols) + 16 * (cn ^ (4 * (k & 3))) + 8 * (r & 1)) & (cols * G::SW - 1);
+            half[e] = __builtin_bit_cast(
+                u2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tile_s16x4 *)(region + o)));
+        }
+        return u4v{half[0].x, half[0].y, half[1].x, half[1].y};
+    };
     auto read = [&](Frag &R, auto k, int u, auto kkc, const Frag *prev) {
         constexpr int kk = decltype(kkc)::value;
         constexpr int h = kk % G::SUB;
@@ -421,36 +459,22 @@ void mx_gemm_tile(GemmArgs p)
             // super-stage, like E2M1; with no scale codes any fixed K order
             // shared by A and B computes the product)
             const int c = F == FMT_FP8 ? 4 * h + 2 * v + g : h + 4 * g;
+            if constexpr (TA) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-                R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
+                for (int i = 0; i < MT; ++i) {
+                    const int cm = 4 * (wm * MT + i) + 2 * (r >> 4) + ((r & 3) >> 1);   // column chunk
+                    R.a[i][v] = read_kmajor(slot, G::BM, cm, c);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    R.a[i][v] = *reinterpret_cast<const u4v *>(slot + G::code_off(arow + 32 * i, c));
+            }
             if constexpr (TB) {
-                // B stored [K][N], read transposed: for each group of 16
-                // lanes the instruction takes four K rows of 16 columns,
-                // lanes 4i .. 4i+3 giving row i's four 8-byte pieces, and
-                // hands lane t of the group column t of the four rows.  Lane
-                // (r, g) thus gets column r of the fragment at K rows
-                // 8c .. 8c+3 from one read and 8c+4 .. 8c+7 from another
-                // (c = h + 4g, the K values its A fragment holds).
-                const char *bs = slot + G::BM * G::SW;
-                const int jr = (r & 15) >> 2;
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int cn = 4 * (wn * NT + j) + 2 * (r >> 4) + ((r & 3) >> 1);   // column chunk
-                    u2v half[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int k = 8 * c + 4 * e + jr;
-                        // (the mask, a no-op here, bounds the offset to the B
-                        // region: the compiler then sees which slot the read
-                        // touches and does not wait for loads into the other)
-                        const int o = (k * (2 * G::BN) + 16 * (cn ^ (4 * (k & 3))) + 8 * (r & 1)) & (G::BN * G::SW - 1);
-                        const char *a = bs + o;
-                        half[e] = __builtin_bit_cast(
-                            u2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                     (__attribute__((address_space(3))) tile_s16x4 *)(a)));
-                    }
-                    R.b[j][v] = u4v{half[0].x, half[0].y, half[1].x, half[1].y};
+                    R.b[j][v] = read_kmajor(slot + G::BM * G::SW, G::BN, cn, c);
                 }
             } else {
 #pragma unroll
@@ -517,7 +541,7 @@ void mx_gemm_tile(GemmArgs p)
     };
 
     constexpr int NM = MT * NT;                  // MFMAs per sub-step
-    constexpr int NCR = NV * (MT + (TB ? 2 : 1) * NT);   // fragment reads per sub-step
+    constexpr int NCR = NV * ((TA ? 2 : 1) * MT + (TB ? 2 : 1) * NT);   // fragment reads per sub-step
     Frag R[2];
 
     // prologue: period 0's scale codes written, the next staged;

@@ -719,15 +719,16 @@ const DenseFn kDense[2][2][2][3] = {MXG_DLAYOUTS(DENSE_BF16), MXG_DLAYOUTS(DENSE
 // NT (both operands K-contiguous, the MFMA's own layout): the tile kernel
 // with 16-bit operands (its loads, LDS slots and pipeline; no scale codes).
 // [dtype][tile: 256x256, 128x256, 128x128][out]
-// NN (B stored [K][N]): the same with B's slots K-row-major, read with
-// transposing LDS reads (TB).  [layout: NT, NN][dtype][tile][out]
-#define MXG_D16(F, MT, NT, TB)                                                                   \
-    {&mx_gemm_tile<F, MT, NT, OUT_BF16, 0, 0, 2, TB>, &mx_gemm_tile<F, MT, NT, OUT_F16, 0, 0, 2, TB>, \
-     &mx_gemm_tile<F, MT, NT, OUT_F32, 0, 0, 2, TB>}
-#define MXG_D16T(TB)                                                                             \
-    {{MXG_D16(FMT_BF16, 4, 4, TB), MXG_D16(FMT_BF16, 2, 4, TB), MXG_D16(FMT_BF16, 2, 2, TB)},    \
-     {MXG_D16(FMT_F16, 4, 4, TB), MXG_D16(FMT_F16, 2, 4, TB), MXG_D16(FMT_F16, 2, 2, TB)}}
-const KernelFn kDenseTile[2][2][3][3] = {MXG_D16T(0), MXG_D16T(1)};
+// The other layouts: an operand contiguous along M or N gets slots of K
+// rows, read with transposing LDS reads (TA: A stored [K][M]; TB: B stored
+// [K][N]).  [trans_a][trans_b][dtype][tile][out]
+#define MXG_D16(F, MT, NT, TB, TA)                                                               \
+    {&mx_gemm_tile<F, MT, NT, OUT_BF16, 0, 0, 2, TB, TA>,                                       \
+     &mx_gemm_tile<F, MT, NT, OUT_F16, 0, 0, 2, TB, TA>, &mx_gemm_tile<F, MT, NT, OUT_F32, 0, 0, 2, TB, TA>}
+#define MXG_D16T(TB, TA)                                                                         \
+    {{MXG_D16(FMT_BF16, 4, 4, TB, TA), MXG_D16(FMT_BF16, 2, 4, TB, TA), MXG_D16(FMT_BF16, 2, 2, TB, TA)}, \
+     {MXG_D16(FMT_F16, 4, 4, TB, TA), MXG_D16(FMT_F16, 2, 4, TB, TA), MXG_D16(FMT_F16, 2, 2, TB, TA)}}
+const KernelFn kDenseTile[2][2][2][3][3] = {{MXG_D16T(1, 0), MXG_D16T(0, 0)}, {MXG_D16T(1, 1), MXG_D16T(0, 1)}};
 
 // The largest of the three tiles that still gives at least 192 workgroups
 // (the same rule as the MX products'), else 128 x 128.
@@ -762,10 +763,11 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
         return MXG_ERR_SHAPE;
     if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
         return MXG_ERR_PTR_ALIGN;
-    // NT, and NN where B's offsets stay below 2^31 (64 K rows past K of
-    // N columns): the tile kernel
-    const bool nn_tile = !trans_a && !trans_b && 2 * N * (K + 64) < ((int64_t)1 << 31);
-    if ((!trans_a && trans_b) || nn_tile) {
+    // the tile kernel where the offsets into an operand stored [K][M] or
+    // [K][N] stay below 2^31 (64 K rows past K of M or N columns)
+    const bool a_ok = !trans_a || 2 * M * (K + 64) < ((int64_t)1 << 31);
+    const bool b_ok = trans_b || 2 * N * (K + 64) < ((int64_t)1 << 31);
+    if (a_ok && b_ok) {
         const int t = dense_nt_tile(M, N);
         const int bm = t == 0 ? 256 : 128, bn = t == 2 ? 128 : 256;
         const int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
@@ -784,7 +786,7 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
         p.row_bytes = (unsigned)(2 * K);
         p.kbytes = p.row_bytes;
         p.splits = 1;
-        hipLaunchKernelGGL(kDenseTile[nn_tile ? 1 : 0][dtype][t][out_dtype], dim3((unsigned)tiles), dim3(256), 0,
+        hipLaunchKernelGGL(kDenseTile[trans_a][trans_b][dtype][t][out_dtype], dim3((unsigned)tiles), dim3(256), 0,
                            stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {

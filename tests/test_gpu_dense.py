@@ -112,21 +112,22 @@ def test_large_sampled(mx):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("tb", [1, 0], ids=["NT", "NN"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=["NN", "NT", "TN", "TT"])
 @pytest.mark.parametrize("shape", [(4096, 3072, 264), (2048, 3072, 520), (1000, 1000, 72)],
                          ids=["256x256tile", "128x256tile", "128x128tile"])
-def test_tile_layouts_sampled(mx, dtype, tb, shape):
-    # NT and NN run on the tile kernel (NN with B's slots K-row-major, read
-    # transposed), on the 256 x 256, 128 x 256 or 128 x 128 tile by the
-    # number of output tiles; K not a multiple of the 64-deep super-stage;
-    # sampled outputs plus the last row and column against the oracle
+def test_tile_layouts_sampled(mx, dtype, ta, tb, shape):
+    # every layout runs on the tile kernel (an operand stored [K][M] or
+    # [K][N] with slots of K rows, read transposed), on the 256 x 256,
+    # 128 x 256 or 128 x 128 tile by the number of output tiles; K not a
+    # multiple of the 64-deep super-stage; sampled outputs plus the last row
+    # and column against the oracle
     M, N, K = shape
-    rng = np.random.default_rng(M + N + K + tb)
-    A = bits(rng.standard_normal((M, K)), dtype)
+    rng = np.random.default_rng(M + N + K + 2 * ta + tb)
+    A = bits(rng.standard_normal((M, K)), dtype)            # the logical [M][K] operand
     B = bits(rng.standard_normal((K, N)), dtype)            # the logical [K][N] operand
-    b_st = stored(B, tb)
-    print("dense tile", dtype, "NT" if tb else "NN", shape, flush=True)
-    c32 = run(mx, dtype, 0, tb, A, b_st, M, N, K, "f32")
+    a_st, b_st = stored(A, ta), stored(B, tb)
+    print("dense tile", dtype, "NT"[ta] + "NT"[tb], shape, flush=True)
+    c32 = run(mx, dtype, ta, tb, a_st, b_st, M, N, K, "f32")
     ms = np.concatenate([rng.integers(0, M, 3000), np.full(64, M - 1), rng.integers(0, M, 64)])
     ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, 64), np.full(64, N - 1)])
     Av = oracle.dense_values(dtype, A, (M, K))
@@ -136,5 +137,5 @@ def test_tile_layouts_sampled(mx, dtype, tb, shape):
     tol = (K / 16 + 16) * 2.0 ** -24 * S + 2.0 ** -126 * K
     assert np.all(np.abs(c32[ms, ns] - ref) <= tol)
     for out, rnd in (("bf16", oracle.round_bf16), ("f16", oracle.round_f16)):
-        b16 = run(mx, dtype, 0, tb, A, b_st, M, N, K, out)
+        b16 = run(mx, dtype, ta, tb, a_st, b_st, M, N, K, out)
         assert np.array_equal(b16, rnd(c32)), "%s %s != RNE(f32)" % (shape, out)
