@@ -763,10 +763,12 @@ int run_dense(int dtype, int trans_a, int trans_b, const void *a, const void *b,
         return MXG_ERR_SHAPE;
     if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
         return MXG_ERR_PTR_ALIGN;
-    // the tile kernel where the offsets into an operand stored [K][M] or
-    // [K][N] stay below 2^31 (64 K rows past K of M or N columns)
-    const bool a_ok = !trans_a || 2 * M * (K + 64) < ((int64_t)1 << 31);
-    const bool b_ok = trans_b || 2 * N * (K + 64) < ((int64_t)1 << 31);
+    // the tile kernel where its 32-bit offsets into an operand stored [K][M]
+    // or [K][N] cannot wrap (a super-stage's 64 K rows past a live one's
+    // start, M or N columns each); else (only with K < 64 and 2^24 or more
+    // columns) the transposing kernel
+    const bool a_ok = !trans_a || 2 * M * (K + 64) < ((int64_t)1 << 32);
+    const bool b_ok = trans_b || 2 * N * (K + 64) < ((int64_t)1 << 32);
     if (a_ok && b_ok) {
         const int t = dense_nt_tile(M, N);
         const int bm = t == 0 ? 256 : 128, bn = t == 2 ? 128 : 256;

@@ -139,3 +139,20 @@ def test_tile_layouts_sampled(mx, dtype, ta, tb, shape):
     for out, rnd in (("bf16", oracle.round_bf16), ("f16", oracle.round_f16)):
         b16 = run(mx, dtype, ta, tb, a_st, b_st, M, N, K, out)
         assert np.array_equal(b16, rnd(c32)), "%s %s != RNE(f32)" % (shape, out)
+
+
+def test_wide_k_major_operand_fallback(mx):
+    # B stored [K][N] with 2^25 columns and K = 8: the tile kernel's 32-bit
+    # offsets could wrap, so the transposing kernel runs it (sampled outputs,
+    # the last columns included, exact: small integers)
+    M, N, K = 8, 1 << 25, 8
+    rng = np.random.default_rng(17)
+    Ai = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (K, N), dtype=np.int8)
+    A = bits(Ai, "bf16")
+    B = (Bi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # small integers: exact in BF16
+    print("dense fallback NN", (M, N, K), flush=True)
+    c32 = run(mx, "bf16", 0, 0, A, B, M, N, K, "f32")
+    ns = np.concatenate([rng.integers(0, N, 4000), np.arange(N - 64, N)])
+    ref = Ai.astype(np.int64) @ Bi[:, ns].astype(np.int64)
+    assert np.array_equal(c32[:, ns], ref.astype(np.float64))
