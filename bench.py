@@ -57,7 +57,8 @@ def parse():
                     help="time mx_scaled_mm_fused instead: activation none|relu|silu|gelu, "
                          "bias 0|1, output bf16|mxfp8|mxfp4 (e.g. silu,1,mxfp4)")
     ap.add_argument("--config", default=None, metavar="VARIANT[:PARTS]",
-                    help="force a kernel variant (by name) and K-part count instead of the default")
+                    help="force a kernel variant (by name) and K-part count instead of the default; "
+                         "with --epilogue, a fused variant by name")
     ap.add_argument("--variant", type=int, default=None,
                     help="grouped workloads: kernel variant index (default: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -568,7 +569,7 @@ class GemmRunner:
         self.out_bytes = 2.0                 # bytes of C per output element
         self.epi = None
         variant, self.splits = mx.mx_default_config(is_fp4, cs.M, cs.N, cs.K)
-        if config:
+        if config and not epilogue:
             name, _, sp = config.partition(":")
             variant = next(v for v in range(mx.mx_num_variants()) if mx.mx_variant_name(v) == name)
             self.splits = int(sp or 1)
@@ -592,12 +593,16 @@ class GemmRunner:
             bias_ptr = self.bias.data_ptr() if self.bias is not None else None
             csp = [t.data_ptr() if t is not None else None for t in c_scales]
             self.epi = {"act": act_s, "bias": bias_s == "1", "out": out_s}
-            self.kernel = mx.mx_fused_variant_name(mx.mx_fused_default_variant(is_fp4, cs.M, cs.N, cs.K))
+            fv = mx.mx_fused_default_variant(is_fp4, cs.M, cs.N, cs.K)
+            if config:   # a fused variant by name (no K parts in the fused kernels)
+                fv = next(v for v in range(mx.mx_fused_num_variants())
+                          if mx.mx_fused_variant_name(v) == config.partition(":")[0])
+            self.kernel = mx.mx_fused_variant_name(fv)
 
             def step(i):
                 a, b, sa, sb, c = ptrs[i % R]
                 rc = fused(1 if is_fp4 else 0, a, b, sa, sb, bias_ptr, act, c, csp[i % R], cs.M, cs.N,
-                           cs.K, out_kind, -1, st_ptr)
+                           cs.K, out_kind, fv, st_ptr)
                 if rc:
                     raise mx.MxGemmError(rc, "bench step")
         elif config:
