@@ -402,12 +402,68 @@ def mx_dense_gemm(a, b, c, M, N, K, trans_a=0, trans_b=0, dtype=None, out_dtype=
 
 
 # ------------------------------------------------------------- convenience
-def scaled_mm(a, b, a_scale, b_scale, fmt: str, M: int, N: int, K: int,
-              out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
-    """C = MX scaled GEMM of packed operands (fmt 'fp4' or 'fp8'); returns [M, N]."""
-    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+_FMT_OF_DTYPE = {}
+for _name, _fmt in (("float4_e2m1fn_x2", "fp4"), ("float8_e4m3fn", "fp8")):
+    if hasattr(torch, _name):
+        _FMT_OF_DTYPE[getattr(torch, _name)] = _fmt
+
+
+def _nk_storage(t):
+    """A 2-D operand given as stored [rows][cols] (contiguous), or as the
+    column-major [cols][rows] view of that storage (what F.scaled_mm takes as
+    its second operand): the contiguous [rows][cols] tensor."""
+    if t.dim() != 2:
+        raise ValueError("operands must be 2-D")
+    if t.is_contiguous():
+        return t
+    if t.t().is_contiguous():
+        return t.t()
+    raise ValueError("operand must be contiguous or the transpose of a contiguous tensor")
+
+
+def scaled_mm_shapes(a, b, a_scale, b_scale, fmt=None):
+    """(fmt, M, N, K, a, b, a_scale, b_scale) of a scaled_mm call with 2-D
+    operands: a [M][K/2] (E2M1 pairs) or [M][K] (E4M3) bytes, row-major; b
+    [N][K/2] / [N][K] bytes, or its column-major [K/2][N] / [K][N] view; the
+    scales [M][K/32] and [N][K/32] (or that one's transpose view).  fmt
+    'fp4' / 'fp8', or None to take it from a's dtype."""
+    if fmt is None:
+        fmt = _FMT_OF_DTYPE.get(a.dtype)
+        if fmt is None:
+            raise ValueError("fmt is required unless a is float4_e2m1fn_x2 or float8_e4m3fn")
+    if fmt not in ("fp4", "fp8"):
+        raise ValueError("fmt must be 'fp4' or 'fp8'")
+    a, b = _nk_storage(a), _nk_storage(b)
+    a_scale, b_scale = _nk_storage(a_scale), _nk_storage(b_scale)
+    M, kb = a.shape
+    N = b.shape[0]
+    K = kb * 2 if fmt == "fp4" else kb
+    if b.shape[1] != kb:
+        raise ValueError("a and b disagree on K")
+    if tuple(a_scale.shape) != (M, K // 32) or tuple(b_scale.shape) != (N, K // 32):
+        raise ValueError("scales must be [M][K/32] and [N][K/32]")
+    return fmt, int(M), int(N), int(K), a, b, a_scale, b_scale
+
+
+def scaled_mm(a, b, a_scale, b_scale, fmt=None, M=None, N=None, K=None,
+              out_dtype=torch.bfloat16, workspace="auto", stream=None) -> torch.Tensor:
+    """C = MX scaled GEMM of packed operands; returns a new [M, N] tensor.
+
+    With M, N and K given, the operands are any 1-byte CUDA tensors (or raw
+    pointers) laid out as mx_scaled_mm_fp4 / mx_scaled_mm_fp8 take them and
+    fmt ('fp4' or 'fp8') is required.  Without them, the operands are 2-D
+    tensors whose shapes give the sizes (scaled_mm_shapes): torch's
+    float4_e2m1fn_x2 / float8_e4m3fn codes and float8_e8m0fnu scales, or
+    uint8 with fmt, B either stored [N][K] or as F.scaled_mm's column-major
+    [K][N] view of that storage."""
+    if M is None or N is None or K is None:
+        fmt, M, N, K, a, b, a_scale, b_scale = scaled_mm_shapes(a, b, a_scale, b_scale, fmt)
+    elif fmt not in ("fp4", "fp8"):
+        raise ValueError("fmt must be 'fp4' or 'fp8'")
+    dev = a.device if isinstance(a, torch.Tensor) else torch.device("cuda")
+    c = torch.empty((M, N), dtype=out_dtype, device=dev)
     fn = mx_scaled_mm_fp4 if fmt == "fp4" else mx_scaled_mm_fp8
-    fn(a, b, a_scale, b_scale, c, M, N, K, stream=stream)
+    fn(a, b, a_scale, b_scale, c, M, N, K, workspace=workspace, stream=stream)
     return c
 
 

@@ -295,6 +295,26 @@ def test_streams(mx):
         mxcheck.check_f32(c32, cref, S, K, None, "stream %s %d" % (fmt, N))
 
 
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_scaled_mm_typed_operands(mx, fmt):
+    # torch's MX dtypes, sizes taken from the shapes and B given as
+    # F.scaled_mm's column-major K x N view: the same bits as the explicit
+    # entry point on the same bytes, and the oracle's bound
+    M, N, K = 40, 456, 1536
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=77)
+    code = torch.float4_e2m1fn_x2 if fmt == "fp4" else torch.float8_e4m3fn
+    kb = K // 2 if fmt == "fp4" else K
+    da, db = dev(a).view(M, kb).view(code), dev(b).view(N, kb).view(code)
+    dsa = dev(sa).view(M, K // 32).view(torch.float8_e8m0fnu)
+    dsb = dev(sb).view(N, K // 32).view(torch.float8_e8m0fnu)
+    c = mx.scaled_mm(da, db.t(), dsa, dsb.t(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = run(mx, fmt, a, b, sa, sb, M, N, K, "f32")
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
+    cref, S = oracle.gemm(fmt, a, b, sa, sb, M, N, K)
+    mxcheck.check_f32(ref, cref, S, K, None, "scaled_mm %s" % fmt)
+
+
 def test_one_hip_runtime_in_process(mx):
     maps = open("/proc/self/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
