@@ -9,6 +9,13 @@
         per-kernel average of every counter in the *_counter_collection.csv
         files that ``rocprofv3 --pmc ... --output-format csv -d DIR`` writes;
 
+    python -m block_scaled_precision_mm_amd.profsum vs-aten DIR LOG
+        device time per call of ATen's MX product and of this library's, shape
+        by shape, from the kernel trace of ``python3 -m
+        block_scaled_precision_mm_amd.vs_aten > LOG`` run under ``rocprofv3
+        --kernel-trace --output-format csv -d DIR``, and the geometric mean of
+        the ratio per format;
+
     python -m block_scaled_precision_mm_amd.profsum traffic --workload W --kernel-match S \\
             --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes B
         HBM bytes per launch of the kernel whose name contains S: FETCH_SIZE
@@ -23,6 +30,7 @@ import argparse
 import csv
 import glob
 import json
+import math
 import os
 import sys
 from collections import defaultdict
@@ -78,6 +86,36 @@ def _one(cmap, match, counter):
     return hits[0][1]
 
 
+def vs_aten(d, log):
+    """Rows (fmt, M, N, K, aten_us, lib_us, aten_kernels_per_call, aten_kernel,
+    max_diff_over_max) and the shapes ATen rejected; phases are the kernels
+    between two launches of the library's empty kernel, ATen's then the
+    library's for each timed shape of the log."""
+    recs = [json.loads(l) for l in open(log) if l.startswith("{")]
+    timed = [r for r in recs if "calls" in r]
+    trace = sorted(_rows(d, "_kernel_trace.csv"), key=lambda r: int(_col(r, "Start_Timestamp")))
+    phases, cur, inside = [], [], False
+    for r in trace:
+        if "mx_empty_kernel" in _col(r, "Kernel_Name"):
+            if inside:
+                phases.append(cur)
+            cur, inside = [], not inside
+        elif inside:
+            cur.append(r)
+    if len(phases) != 2 * len(timed):
+        raise SystemExit("expected %d phases, found %d" % (2 * len(timed), len(phases)))
+    rows = []
+    for k, r in enumerate(timed):
+        t = []
+        for ph in phases[2 * k: 2 * k + 2]:
+            ns = sum(int(_col(x, "End_Timestamp")) - int(_col(x, "Start_Timestamp")) for x in ph)
+            t.append(ns / r["calls"] / 1e3)
+        names = sorted({_col(x, "Kernel_Name") for x in phases[2 * k]})
+        rows.append((r["fmt"], r["M"], r["N"], r["K"], t[0], t[1], len(phases[2 * k]) / r["calls"],
+                     names[0] if len(names) == 1 else "%d kernels" % len(names), r["max_diff_over_max"]))
+    return rows, [r for r in recs if "aten_error" in r]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -92,7 +130,28 @@ def main(argv=None):
     t.add_argument("--copy-match", default="copyBuffer", help="name of the copy kernel")
     t.add_argument("--kernel-name", default=None, help="variant name recorded with the figure")
     t.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    v = sub.add_parser("vs-aten")
+    v.add_argument("dir")
+    v.add_argument("log")
     args = ap.parse_args(argv)
+
+    if args.cmd == "vs-aten":
+        rows, rejected = vs_aten(args.dir, args.log)
+        print("%-4s %5s %6s %6s %10s %10s %7s  %-9s %s" % ("fmt", "M", "N", "K", "aten_us", "lib_us",
+                                                            "ratio", "diff/max", "ATen kernel"))
+        seen, logs = set(), defaultdict(list)
+        for fmt, M, N, K, ta, tl, kpc, kname, diff in rows:
+            print("%-4s %5d %6d %6d %10.2f %10.2f %7.2f  %.1e  %s (%.1f per call)" % (
+                fmt, M, N, K, ta, tl, ta / tl, diff, kname[:48], kpc))
+            if (fmt, M, N, K) not in seen:
+                seen.add((fmt, M, N, K))
+                logs[fmt].append(math.log(ta / tl))
+        for fmt, lv in sorted(logs.items()):
+            print("%s: geometric mean of ATen time / library time over %d shapes: %.3f" % (
+                fmt, len(lv), math.exp(sum(lv) / len(lv))))
+        for r in rejected:
+            print("not taken by ATen: %s %dx%dx%d (%s)" % (r["fmt"], r["M"], r["N"], r["K"], r["aten_error"]))
+        return
 
     if args.cmd == "kernels":
         print("%-100s %6s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
