@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated operand sets (0 = one set, cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-aten", action="store_true",
+                    help="skip timing ATen's MX scaled GEMM beside the headline")
     ap.add_argument("--no-sub-workloads", action="store_true",
                     help="time only --workload (by default the other named workloads c1-c4 are "
                          "timed in the same process and reported under per_workload)")
@@ -791,6 +793,49 @@ print(json.dumps(out))
     return res
 
 
+def aten_beside(runner, cs, steps, warmup, lib_ms):
+    """ATen's MX scaled GEMM (torch.nn.functional.scaled_mm with BlockWise1x32
+    E8M0 scales, no swizzle, BF16 output) on the runner's rotated operand
+    sets, timed exactly as the library's calls were (the runner's timing
+    loop with ATen's call as the step): the pages quote their kernels as
+    speedups over it.  Context for the headline, not part of it; None-like
+    record when this torch has no such path or ATen rejects the shape."""
+    import torch
+    import torch.nn.functional as F
+    rec = {"op": "torch.nn.functional.scaled_mm, BlockWise1x32 both operands, no swizzle, bf16 out",
+           "torch": torch.__version__}
+    if cs.M % 32 or cs.N % 32:
+        rec["error"] = "ATen takes M and N multiples of 32 only"
+        return rec
+    kb = cs.K // 2 if cs.fmt == "fp4" else cs.K
+    try:
+        code = torch.float4_e2m1fn_x2 if cs.fmt == "fp4" else torch.float8_e4m3fn
+        ops = [(s_[0].view(cs.M, kb).view(code), s_[1].view(cs.N, kb).view(code),
+                s_[2].view(cs.M, cs.K // 32).view(torch.float8_e8m0fnu),
+                s_[3].view(cs.N, cs.K // 32).view(torch.float8_e8m0fnu)) for s_ in runner.sets]
+        bw = F.ScalingType.BlockWise1x32
+        nos = F.SwizzleType.NO_SWIZZLE
+
+        def step(i):
+            a, b, sa, sb = ops[i % len(ops)]
+            F.scaled_mm(a, b.t(), sa, bw, sb, bw, swizzle_a=nos, swizzle_b=nos, output_dtype=torch.bfloat16)
+
+        step(0)
+        torch.cuda.synchronize()
+    except Exception as e:   # no MX path in this torch, or the shape is rejected
+        rec["error"] = str(e).splitlines()[0][:200]
+        return rec
+    lib_step = runner.step
+    runner.step = step
+    try:
+        ams, _, _ = runner.time(steps, warmup)
+    finally:
+        runner.step = lib_step
+    rec["us_per_call"] = round(ams * 1e3, 3)
+    rec["aten_time_over_lib_time"] = round(ams / lib_ms, 3)
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -861,6 +906,8 @@ def main():
             f = min(load) / 2400.0
             roof["peak_at_sclk"] = round(roof["peak"] * f, 1)
             roof["frac_at_sclk"] = round(roof["achieved"] / roof["peak_at_sclk"], 4)
+    if not (args.no_aten or args.epilogue or args.config):
+        out["aten"] = aten_beside(runner, cs, args.steps, args.warmup, ms)
     del runner
     torch.cuda.empty_cache()
 
