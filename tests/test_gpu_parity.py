@@ -315,6 +315,36 @@ def test_scaled_mm_typed_operands(mx, fmt):
     mxcheck.check_f32(ref, cref, S, K, None, "scaled_mm %s" % fmt)
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("fp4", 32, 14336, 4096), ("fp8", 64, 4096, 4096),
+                                        ("fp4", 256, 4096, 8192), ("fp8", 96, 160, 640)])
+def test_same_op_as_torch_scaled_mm(mx, fmt, M, N, K):
+    # torch's own F.scaled_mm with BlockWise1x32 E8M0 scales (the op the
+    # pages name) on the same codes: the two differ only in summation order,
+    # so by at most one BF16 ulp of the largest output (2^-7 of it; allowed
+    # 2^-6).  Skipped where this torch has no MX path.
+    F = torch.nn.functional
+    if not hasattr(F, "scaled_mm") or not hasattr(F, "ScalingType"):
+        pytest.skip("torch has no F.scaled_mm")
+    a, b, sa, sb = quantized(fmt, M, N, K, seed=M + K)
+    code = torch.float4_e2m1fn_x2 if fmt == "fp4" else torch.float8_e4m3fn
+    kb = K // 2 if fmt == "fp4" else K
+    da, db = dev(a).view(M, kb).view(code), dev(b).view(N, kb).view(code)
+    dsa = dev(sa).view(M, K // 32).view(torch.float8_e8m0fnu)
+    dsb = dev(sb).view(N, K // 32).view(torch.float8_e8m0fnu)
+    try:
+        ref = F.scaled_mm(da, db.t(), dsa, F.ScalingType.BlockWise1x32, dsb, F.ScalingType.BlockWise1x32,
+                          swizzle_a=F.SwizzleType.NO_SWIZZLE, swizzle_b=F.SwizzleType.NO_SWIZZLE,
+                          output_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+    except (RuntimeError, NotImplementedError) as e:
+        pytest.skip("this torch does not run MX F.scaled_mm: %s" % str(e).splitlines()[0][:120])
+    c = mx.scaled_mm(da, db.t(), dsa, dsb.t())
+    torch.cuda.synchronize()
+    x, y = ref.float().cpu().numpy(), c.float().cpu().numpy()
+    assert np.isfinite(y).all() and np.isfinite(x).all()
+    assert np.abs(x - y).max() <= 2.0 ** -6 * np.abs(y).max(), (fmt, M, N, K)
+
+
 def test_one_hip_runtime_in_process(mx):
     maps = open("/proc/self/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
