@@ -152,8 +152,9 @@ void mx_gemm_stream(GemmArgs p)
         m0 = local * (16 * MT);
     }
     const int n0 = blockIdx.x * (16 * WN);
-    // split-K across workgroups: this workgroup's K part (whole groups)
-    if constexpr (!GRP && !EPI)
+    // split-K across workgroups: this workgroup's K part (whole groups);
+    // only with KW > 1, whose epilogue holds the cross-workgroup reduction
+    if constexpr (!GRP && !EPI && KW > 1)
         select_split<F>(p, 4);
 
     // Buffers over this workgroup's rows (and K part) only: rows past M or

@@ -54,9 +54,11 @@ constexpr int ring_depth(int fmt, int mt, int wn)
 #define MXG_SFN(F, MT, WN, KW, O) (&mx_gemm_stream<F, MT, WN, KW, ring_depth(F, MT, WN), O>)
 #define MXG_SOUTS(F, MT, WN, KW) \
     {MXG_SFN(F, MT, WN, KW, OUT_BF16), MXG_SFN(F, MT, WN, KW, OUT_F16), MXG_SFN(F, MT, WN, KW, OUT_F32)}
+// (split-K across workgroups only with KW > 1: its reduction runs on the
+// workgroup's LDS-summed tile)
 #define MXG_STREAM(MT, WN, KW)                                                        \
     {"stream_" #MT "x" #WN "_k" #KW, 16 * MT, 16 * WN, 64 * KW,                        \
-     {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0, 1}
+     {MXG_SOUTS(FMT_FP8, MT, WN, KW), MXG_SOUTS(FMT_FP4, MT, WN, KW)}, {0, 0}, 0, (KW) > 1}
 
 // Decode kernel: A tile of MT subtiles and all scale codes resident in LDS
 // (K up to K8 / K4 for FP8 / FP4), NW groups of 16 B rows, each streamed by
@@ -88,6 +90,8 @@ const Variant kVariants[] = {
     MXG_STREAM(2, 2, 4),
     MXG_STREAM(2, 4, 8),
     MXG_STREAM(4, 2, 8),
+    MXG_STREAM(2, 1, 1),
+    MXG_STREAM(2, 1, 2),
     //          name              MT NW G  KS K4    K8    DMA
     MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048, 1),
     MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048, 1),
@@ -323,8 +327,16 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
         return find_variant("stream_1x1_k16");
     if (M <= 16)
         return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
-    if (M <= 32)
-        return find_variant(N >= 8192 ? "stream_2x4_k8" : "stream_2x1_k4");
+    // 17-32 rows on narrow N: as many waves splitting K as the row is long
+    // (one up to 256 bytes per row, two up to 1024, else four; E2M1
+    // 32 x 256 x 256: 3.14 us against 3.58 with four, 32 x 1024 x 2048:
+    // 4.10 against 4.58; E4M3 32 x 4096 x 512: 3.68 against 4.15, at
+    // 32 x 1024 x 2048 four waves stay ahead, 5.04 against 5.34)
+    if (M <= 32) {
+        const int64_t rb = is_fp4 ? K / 2 : K;
+        return find_variant(N >= 8192 ? "stream_2x4_k8"
+                            : rb <= 256 ? "stream_2x1_k1" : rb <= 1024 ? "stream_2x1_k2" : "stream_2x1_k4");
+    }
     // 33-64 rows on wide N: the 64 x 64 four-slot tile (64 x 14336 x 4096:
     // 11.7 us against 14.9 on a 64 x 64 split-K tile of register rings,
     // 64 x 25600 x 5120 24.8 against 32.7, E4M3 48 x 28672 x 4096 29.4

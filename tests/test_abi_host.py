@@ -341,6 +341,11 @@ DEFAULTS = [
     (0, 32, 14336, 4096, "stream_2x4_k8"),     # E4M3 decode widths stay on the stream kernel
     (0, 8, 14336, 4096, "stream_1x2_k4"),
     (1, 32, 4096, 4096, "stream_2x1_k4"),
+    (1, 32, 256, 256, "stream_2x1_k1"),      # one wave per K up to 256 bytes per row
+    (0, 24, 1024, 256, "stream_2x1_k1"),
+    (1, 32, 1024, 2048, "stream_2x1_k2"),    # two up to 1024
+    (0, 32, 4096, 1024, "stream_2x1_k2"),
+    (0, 32, 1024, 2048, "stream_2x1_k4"),
     (0, 64, 4096, 4096, "stream_2x2_k4"),
     (1, 64, 14336, 4096, "tile_64x64_r4"),
     (0, 48, 28672, 4096, "tile_64x64_r4"),
