@@ -92,6 +92,8 @@ const Variant kVariants[] = {
     MXG_STREAM(4, 2, 8),
     MXG_STREAM(2, 1, 1),
     MXG_STREAM(2, 1, 2),
+    MXG_STREAM(1, 1, 1),
+    MXG_STREAM(1, 1, 2),
     //          name              MT NW G  KS K4    K8    DMA
     MXG_DECODE("decode_32x64",    2, 4, 3, 1, 4096, 2048, 1),
     MXG_DECODE("decode_16x64",    1, 4, 3, 1, 4096, 2048, 1),
@@ -325,8 +327,17 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     // 10.3 with four)
     if (M <= 16 && is_fp4 && K >= 8192)
         return find_variant("stream_1x1_k16");
-    if (M <= 16)
-        return find_variant(N >= 8192 && !is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
+    // 1-16 rows on narrow N: one wave per K up to K = 1024, two up to 2048
+    // (E2M1) / 4096 (E4M3), else four (E2M1 8 x 256 x 512: 2.72 us against
+    // 3.48 with four waves, 8 x 256 x 2048: 3.34 against 3.57, 8 x 4096 x
+    // 4096: 4.47 with four against 4.76 with two; E4M3 8 x 4096 x 512: 3.17
+    // against 3.96, 8 x 4096 x 4096: 5.77 with two against 6.30)
+    if (M <= 16) {
+        if (N >= 8192)
+            return find_variant(!is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
+        return find_variant(K <= 1024 ? "stream_1x1_k1"
+                            : K <= (is_fp4 ? 2048 : 4096) ? "stream_1x1_k2" : "stream_1x1_k4");
+    }
     // 17-32 rows on narrow N: as many waves splitting K as the row is long
     // (one up to 256 bytes per row, two up to 1024, else four; E2M1
     // 32 x 256 x 256: 3.14 us against 3.58 with four, 32 x 1024 x 2048:

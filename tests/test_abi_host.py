@@ -342,6 +342,11 @@ DEFAULTS = [
     (0, 8, 14336, 4096, "stream_1x2_k4"),
     (1, 32, 4096, 4096, "stream_2x1_k4"),
     (1, 32, 256, 256, "stream_2x1_k1"),      # one wave per K up to 256 bytes per row
+    (1, 8, 256, 1024, "stream_1x1_k1"),      # 1-16 rows: one wave up to K = 1024
+    (0, 16, 4096, 512, "stream_1x1_k1"),
+    (1, 1, 4096, 2048, "stream_1x1_k2"),     # two up to 2048 (E2M1) / 4096 (E4M3)
+    (0, 8, 4096, 4096, "stream_1x1_k2"),
+    (1, 8, 4096, 4096, "stream_1x1_k4"),
     (0, 24, 1024, 256, "stream_2x1_k1"),
     (1, 32, 1024, 2048, "stream_2x1_k2"),    # two up to 1024
     (0, 32, 4096, 1024, "stream_2x1_k2"),
