@@ -333,8 +333,10 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     // 4096: 4.47 with four against 4.76 with two; E4M3 8 x 4096 x 512: 3.17
     // against 3.96, 8 x 4096 x 4096: 5.77 with two against 6.30)
     if (M <= 16) {
+        // (E4M3 at K >= 8192: the 64 x 64 four-slot tile, 16 x 14336 x 8192
+        // 25.0 us against 28.7, 8 x 14336 x 8192 26.4 against 27.2)
         if (N >= 8192)
-            return find_variant(!is_fp4 ? "stream_1x2_k4" : "stream_1x1_k4");
+            return find_variant(is_fp4 ? "stream_1x1_k4" : K >= 8192 ? "tile_64x64_r4" : "stream_1x2_k4");
         return find_variant(K <= 1024 ? "stream_1x1_k1"
                             : K <= (is_fp4 ? 2048 : 4096) ? "stream_1x1_k2" : "stream_1x1_k4");
     }
@@ -343,9 +345,14 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     // 32 x 256 x 256: 3.14 us against 3.58 with four, 32 x 1024 x 2048:
     // 4.10 against 4.58; E4M3 32 x 4096 x 512: 3.68 against 4.15, at
     // 32 x 1024 x 2048 four waves stay ahead, 5.04 against 5.34)
+    // 17-32 rows on wide N that the decode kernel does not take (E4M3, or
+    // E2M1 past its K limit): the 64 x 64 four-slot tile (E4M3 32 x 14336 x
+    // 4096: 15.8 us against 19.9 on stream_2x4_k8, 32 x 25600 x 5120: 34.4
+    // against 44.7; E2M1 32 x 14336 x 8192: 16.7 against 18.3, 32 x 25600 x
+    // 8192: 29.2 against 32.4; two K parts slower on each)
     if (M <= 32) {
         const int64_t rb = is_fp4 ? K / 2 : K;
-        return find_variant(N >= 8192 ? "stream_2x4_k8"
+        return find_variant(N >= 8192 ? "tile_64x64_r4"
                             : rb <= 256 ? "stream_2x1_k1" : rb <= 1024 ? "stream_2x1_k2" : "stream_2x1_k4");
     }
     // 33-64 rows on wide N: the 64 x 64 four-slot tile (64 x 14336 x 4096:

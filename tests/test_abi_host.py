@@ -334,11 +334,12 @@ DEFAULTS = [
     (1, 1, 14336, 4096, "stream_1x1_k4"),
     (1, 8, 4096, 14336, "stream_1x1_k16"),
     (1, 1, 4096, 14336, "stream_1x1_k16"),
-    (1, 32, 14336, 8192, "stream_2x4_k8"),     # K past the decode kernel's LDS-resident A tile
+    (1, 32, 14336, 8192, "tile_64x64_r4"),     # K past the decode kernel's LDS-resident A tile
     (1, 32, 25600, 5120, "decode_32x64_k2_long"),
     (1, 16, 14336, 8192, "decode_16x64_k2_long"),
     (1, 128, 4096, 5120, "decode_32x64_k2_long"),
-    (0, 32, 14336, 4096, "stream_2x4_k8"),     # E4M3 decode widths stay on the stream kernel
+    (0, 32, 14336, 4096, "tile_64x64_r4"),     # E4M3 17-32 rows on wide N: the 64 x 64 tile
+    (0, 16, 14336, 8192, "tile_64x64_r4"),     # E4M3 1-16 rows on wide N at K >= 8192
     (0, 8, 14336, 4096, "stream_1x2_k4"),
     (1, 32, 4096, 4096, "stream_2x1_k4"),
     (1, 32, 256, 256, "stream_2x1_k1"),      # one wave per K up to 256 bytes per row
