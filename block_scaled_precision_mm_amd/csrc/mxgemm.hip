@@ -325,8 +325,11 @@ int pick_variant(int is_fp4, int64_t M, int64_t N, int64_t K)
     }
     // long K splits over sixteen waves (8 x 4096 x 14336 E2M1: 8.4 us against
     // 10.3 with four)
+    // (on wide N the 64 x 64 four-slot tile: 1 x 14336 x 8192 15.4 us against
+    // 22.7 on sixteen waves, 16 x 14336 x 10240 19.2 against 27.5, 4 x 25600
+    // x 8192 27.2 against 37.2)
     if (M <= 16 && is_fp4 && K >= 8192)
-        return find_variant("stream_1x1_k16");
+        return find_variant(N >= 8192 ? "tile_64x64_r4" : "stream_1x1_k16");
     // 1-16 rows on narrow N: one wave per K up to K = 1024, two up to 2048
     // (E2M1) / 4096 (E4M3), else four (E2M1 8 x 256 x 512: 2.72 us against
     // 3.48 with four waves, 8 x 256 x 2048: 3.34 against 3.57, 8 x 4096 x

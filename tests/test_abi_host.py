@@ -334,6 +334,8 @@ DEFAULTS = [
     (1, 1, 14336, 4096, "stream_1x1_k4"),
     (1, 8, 4096, 14336, "stream_1x1_k16"),
     (1, 1, 4096, 14336, "stream_1x1_k16"),
+    (1, 1, 14336, 8192, "tile_64x64_r4"),      # long K on wide N: the 64 x 64 tile
+    (1, 16, 14336, 10240, "tile_64x64_r4"),
     (1, 32, 14336, 8192, "tile_64x64_r4"),     # K past the decode kernel's LDS-resident A tile
     (1, 32, 25600, 5120, "decode_32x64_k2_long"),
     (1, 16, 14336, 8192, "decode_16x64_k2_long"),
