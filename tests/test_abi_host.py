@@ -195,6 +195,10 @@ def test_fused_invalid_arguments(lib, args, status):
             assert 0 <= v < n
             # the default always accepts the K it was picked for
             assert shape[2] <= lib.mx_fused_variant_max_k(v, is_fp4)
+    # wide N at 17-64 rows (outside the E2M1 decode widths): the 64 x 64 four-slot tile
+    assert lib.mx_fused_variant_name(lib.mx_fused_default_variant(0, 32, 14336, 4096)) == b"ftile_64x64_r4"
+    assert lib.mx_fused_variant_name(lib.mx_fused_default_variant(1, 32, 14336, 4096)) == b"fdecode_32x64_k2"
+    assert lib.mx_fused_variant_name(lib.mx_fused_default_variant(0, 32, 4096, 4096)) == b"fstream_2x4_k8"
     assert lib.mx_fused_default_variant(1, 0, 8, 128) == -2
     assert lib.mx_fused_default_variant(1, 8, 8, 0) == -2
     assert lib.mx_fused_variant_max_k(n, 1) == -9
